@@ -1,0 +1,161 @@
+"""Thin ctypes binding of ``libnosa.so`` (the C ABI in ``include/nosa.h``).
+
+Argument marshalling only: every function takes device tensors (anything with
+``data_ptr()``), plain integers for pointers, or ``None`` for NULL, forwards them to the
+C entry point of the same name, and raises :class:`NosaError` on a non-zero status.  All
+work runs in the library's HIP kernels; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Any, Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnosa.so")
+
+NOSA_OK, NOSA_EINVAL, NOSA_EUNSUPPORTED, NOSA_ECAPACITY, NOSA_EHIP = 0, -1, -2, -3, -4
+NOSA_F32, NOSA_BF16 = 0, 1
+
+EXPORTED = (
+    "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_block_scores",
+    "nosa_select", "nosa_cache_update", "nosa_sparse_decode",
+)
+
+
+class NosaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("nosa error %d: %s" % (code, message))
+        self.code = code
+
+
+class NosaShape(ctypes.Structure):
+    """Mirror of ``nosa_shape``."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "block_size", "sub_block_size", "n_blocks",
+        "n_blocks_max", "kq", "ke", "cache_slots", "dtype", "decode_splits", "select_parts")]
+
+    def copy(self, **changes) -> "NosaShape":
+        s = NosaShape()
+        ctypes.pointer(s)[0] = self
+        for k, v in changes.items():
+            setattr(s, k, int(v))
+        return s
+
+    def __repr__(self) -> str:
+        return "NosaShape(%s)" % ", ".join("%s=%d" % (n, getattr(self, n)) for n, _ in self._fields_)
+
+
+def make_shape(*, batch, n_q_heads, n_kv_heads, head_dim, n_blocks, kq, ke, n_blocks_max=None,
+               block_size=64, sub_block_size=32, cache_slots=0, dtype=NOSA_BF16, decode_splits=0,
+               select_parts=0) -> NosaShape:
+    s = NosaShape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = batch, n_q_heads, n_kv_heads, head_dim
+    s.block_size, s.sub_block_size, s.n_blocks = block_size, sub_block_size, n_blocks
+    s.n_blocks_max = n_blocks if n_blocks_max is None else n_blocks_max
+    s.kq, s.ke, s.cache_slots, s.dtype = kq, ke, cache_slots, dtype
+    s.decode_splits, s.select_parts = decode_splits, select_parts
+    return s
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnosa.so is not built (%s); run `python -m block_sparse_kv_decode_amd.build` "
+                          "or __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SP = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(NosaShape)
+    L.nosa_last_error.restype = ctypes.c_char_p
+    L.nosa_last_error.argtypes = []
+    L.nosa_version.restype = ctypes.c_char_p
+    L.nosa_version.argtypes = []
+    L.nosa_workspace_bytes.restype = ctypes.c_size_t
+    L.nosa_workspace_bytes.argtypes = [SP]
+    L.nosa_pool_keys.restype = ctypes.c_int
+    L.nosa_pool_keys.argtypes = [SP, P, I32, I32, P, P]
+    L.nosa_block_scores.restype = ctypes.c_int
+    L.nosa_block_scores.argtypes = [SP, P, P, P, P, P]
+    L.nosa_select.restype = ctypes.c_int
+    L.nosa_select.argtypes = [SP, P, P, P, I32, P, P, P, P]
+    L.nosa_cache_update.restype = ctypes.c_int
+    L.nosa_cache_update.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    L.nosa_sparse_decode.restype = ctypes.c_int
+    L.nosa_sparse_decode.argtypes = [SP, P, P, P, I32, P, ctypes.c_float, P, P, P]
+    return L
+
+
+lib = _load()
+
+
+def _p(x: Any) -> Optional[int]:
+    """Pointer of a tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s: Any) -> Optional[int]:
+    """HIP stream handle: None -> torch's current stream on the current device; int -> as is."""
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _check(rc: int) -> None:
+    if rc != NOSA_OK:
+        raise NosaError(rc, lib.nosa_last_error().decode(errors="replace"))
+
+
+def nosa_last_error() -> str:
+    return lib.nosa_last_error().decode(errors="replace")
+
+
+def nosa_version() -> str:
+    return lib.nosa_version().decode()
+
+
+def nosa_workspace_bytes(shape: NosaShape) -> int:
+    n = int(lib.nosa_workspace_bytes(ctypes.byref(shape)))
+    if n == 0:
+        raise NosaError(NOSA_EINVAL, nosa_last_error())
+    return n
+
+
+def nosa_pool_keys(shape, k, first_block, n_new, pooled_k, stream=None) -> None:
+    _check(lib.nosa_pool_keys(ctypes.byref(shape), _p(k), int(first_block), int(n_new), _p(pooled_k),
+                              _stream(stream)))
+
+
+def nosa_block_scores(shape, q, pooled_k, scores, ws, stream=None) -> None:
+    _check(lib.nosa_block_scores(ctypes.byref(shape), _p(q), _p(pooled_k), _p(scores), _p(ws), _stream(stream)))
+
+
+def nosa_select(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, ws, stream=None) -> None:
+    _check(lib.nosa_select(ctypes.byref(shape), _p(q), _p(pooled_k), _p(evict), int(n_blocks_prev),
+                           _p(agn_state), _p(selected), _p(ws), _stream(stream)))
+
+
+def nosa_cache_update(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list,
+                      host_k, host_v, cache_k, cache_v, compute=None, copy=None) -> None:
+    cs = _stream(compute)
+    cp = cs if copy is None else _stream(copy)
+    _check(lib.nosa_cache_update(ctypes.byref(shape), _p(selected), _p(slot_of_block), _p(block_of_slot),
+                                 _p(block_table), _p(miss_cnt), _p(miss_list), _p(host_k), _p(host_v),
+                                 _p(cache_k), _p(cache_v), cs, cp))
+
+
+def nosa_sparse_decode(shape, q, k_store, v_store, store_blocks, block_table, softmax_scale, out, ws,
+                       stream=None) -> None:
+    _check(lib.nosa_sparse_decode(ctypes.byref(shape), _p(q), _p(k_store), _p(v_store), int(store_blocks),
+                                  _p(block_table), float(softmax_scale), _p(out), _p(ws), _stream(stream)))
+
+
+def workspace(shape: NosaShape, device=None):
+    """Zero-filled device workspace of nosa_workspace_bytes(shape) bytes (a torch uint8 tensor)."""
+    import torch
+    return torch.zeros(nosa_workspace_bytes(shape), dtype=torch.uint8, device=device or "cuda")

@@ -1,0 +1,371 @@
+// api.cpp -- the C ABI of include/nosa.h: host-side validation, workspace layout, launch plans.
+//
+// Every entry point validates its arguments on the host before it makes any HIP call, so the
+// error paths run (and are tested) on machines without a GPU.
+#include "nosa.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "nosa_internal.h"
+
+using namespace nosa;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return NOSA_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(NOSA_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Work distribution targets: enough workgroups to give every one of the 256 CUs two of them.
+constexpr int kTargetWorkgroups = 512;
+constexpr int kMinBlocksPerPart = 8;
+
+int check_shape(const nosa_shape *s) {
+    if (!s) return fail(NOSA_EINVAL, "shape is NULL");
+    if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+        return fail(NOSA_EINVAL, "batch, n_q_heads and n_kv_heads must be >= 1");
+    if (s->n_q_heads % s->n_kv_heads != 0)
+        return fail(NOSA_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", s->n_q_heads, s->n_kv_heads);
+    const int G = s->n_q_heads / s->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(NOSA_EUNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(NOSA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+    if (s->block_size != kBlockTokens)
+        return fail(NOSA_EUNSUPPORTED, "block_size must be 64 (got %d)", s->block_size);
+    if (s->sub_block_size != 8 && s->sub_block_size != 16 && s->sub_block_size != 32 && s->sub_block_size != 64)
+        return fail(NOSA_EUNSUPPORTED, "sub_block_size must be 8, 16, 32 or 64 (got %d)", s->sub_block_size);
+    if (s->dtype != NOSA_F32 && s->dtype != NOSA_BF16)
+        return fail(NOSA_EUNSUPPORTED, "dtype must be NOSA_F32 or NOSA_BF16 (got %d)", s->dtype);
+    if (s->kq < 0 || s->ke < 0 || s->kq + s->ke < 1)
+        return fail(NOSA_EINVAL, "budget kq=%d ke=%d: both >= 0 and kq + ke >= 1", s->kq, s->ke);
+    if (s->n_blocks_max < 1 || s->n_blocks_max > kMaxBlocks)
+        return s->n_blocks_max < 1 ? fail(NOSA_EINVAL, "n_blocks_max must be >= 1")
+                                   : fail(NOSA_EUNSUPPORTED, "n_blocks_max %d exceeds %d", s->n_blocks_max, kMaxBlocks);
+    if (s->n_blocks < 1 || s->n_blocks > s->n_blocks_max)
+        return fail(NOSA_EINVAL, "n_blocks %d must lie in [1, n_blocks_max=%d]", s->n_blocks, s->n_blocks_max);
+    if (s->kq + s->ke > s->n_blocks)
+        return fail(NOSA_EINVAL, "budget kq + ke = %d exceeds the %d visible blocks", s->kq + s->ke, s->n_blocks);
+    if (s->decode_splits < 0 || s->select_parts < 0)
+        return fail(NOSA_EINVAL, "decode_splits and select_parts must be >= 0");
+    return NOSA_OK;
+}
+
+int rows_of(const nosa_shape *s) { return s->batch * s->n_kv_heads; }
+int group_of(const nosa_shape *s) { return s->n_q_heads / s->n_kv_heads; }
+int spb_of(const nosa_shape *s) { return s->block_size / s->sub_block_size; }
+size_t elem_bytes(const nosa_shape *s) { return s->dtype == NOSA_BF16 ? 2 : 4; }
+
+struct SplitPlan {
+    int S;     // splits per row
+    int nbs;   // blocks per split
+};
+
+SplitPlan decode_plan(const nosa_shape *s) {
+    const int R = rows_of(s), k = s->kq + s->ke;
+    int S = s->decode_splits > 0 ? s->decode_splits : (kTargetWorkgroups + R - 1) / R;
+    if (S < 1) S = 1;
+    if (S > k) S = k;
+    const int nbs = (k + S - 1) / S;
+    S = (k + nbs - 1) / nbs;   // no empty split
+    return {S, nbs};
+}
+
+struct PartPlan {
+    int P;
+    int bpp;
+};
+
+PartPlan select_plan(const nosa_shape *s) {
+    const int R = rows_of(s), n = s->n_blocks;
+    int P = s->select_parts > 0 ? s->select_parts : (kTargetWorkgroups + R - 1) / R;
+    if (s->select_parts <= 0) {
+        const int cap = n / kMinBlocksPerPart > 0 ? n / kMinBlocksPerPart : 1;
+        if (P > cap) P = cap;
+    }
+    if (P < 1) P = 1;
+    if (P > n) P = n;
+    const int bpp = (n + P - 1) / P;
+    P = (n + bpp - 1) / bpp;
+    return {P, bpp};
+}
+
+struct WsLayout {
+    size_t scores, scnt, part, dcnt, total;
+};
+
+WsLayout ws_layout(const nosa_shape *s) {
+    const size_t R = (size_t)rows_of(s);
+    const SplitPlan dp = decode_plan(s);
+    WsLayout L;
+    size_t off = 0;
+    L.scores = off;
+    off = round_up(off + R * (size_t)s->n_blocks_max * sizeof(float), kAlign);
+    L.scnt = off;
+    off = round_up(off + R * sizeof(uint32_t), kAlign);
+    L.part = off;
+    off = round_up(off + R * (size_t)dp.S * group_of(s) * (size_t)(s->head_dim + 2) * sizeof(float), kAlign);
+    L.dcnt = off;
+    off = round_up(off + R * sizeof(uint32_t), kAlign);
+    L.total = off;
+    return L;
+}
+
+#define REQUIRE_PTR(p, al)                                                                          \
+    do {                                                                                            \
+        if (!(p)) return fail(NOSA_EINVAL, "%s is NULL", #p);                                       \
+        if (!aligned((p), (al))) return fail(NOSA_EINVAL, "%s is not %d-byte aligned", #p, (int)(al)); \
+    } while (0)
+
+// Two events per device order the copy stream after the map update and the compute stream after
+// the transfer.  Created on first use and kept for the life of the process.
+struct DeviceEvents {
+    hipEvent_t mapped = nullptr, copied = nullptr;
+};
+constexpr int kMaxDevices = 64;
+DeviceEvents g_events[kMaxDevices];
+std::mutex g_events_mu;
+
+int get_events(DeviceEvents **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(NOSA_EUNSUPPORTED, "device index %d too large", dev);
+    std::lock_guard<std::mutex> lock(g_events_mu);
+    DeviceEvents &d = g_events[dev];
+    if (!d.mapped) {
+        if ((e = hipEventCreateWithFlags(&d.mapped, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+        if ((e = hipEventCreateWithFlags(&d.copied, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    *out = &d;
+    return NOSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nosa_last_error(void) { return g_err; }
+
+const char *nosa_version(void) { return "nosa-mi355x 0.1 (gfx950)"; }
+
+size_t nosa_workspace_bytes(const nosa_shape *shape) {
+    if (check_shape(shape) != NOSA_OK) return 0;
+    ok();
+    return ws_layout(shape).total;
+}
+
+int nosa_pool_keys(const nosa_shape *shape, const void *k, int32_t first_block, int32_t n_new, float *pooled_k,
+                   hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    REQUIRE_PTR(k, 16);
+    REQUIRE_PTR(pooled_k, 16);
+    if (first_block < 0 || n_new < 0 || (long long)first_block + n_new > shape->n_blocks_max)
+        return fail(NOSA_EINVAL, "blocks [%d, %d) outside [0, n_blocks_max=%d)", first_block,
+                    first_block + n_new, shape->n_blocks_max);
+    if (n_new == 0) return ok();
+    PoolArgs a;
+    a.k = k;
+    a.kp = pooled_k;
+    a.n_blocks_max = shape->n_blocks_max;
+    a.first_block = first_block;
+    a.n_new = n_new;
+    a.spb = spb_of(shape);
+    a.sbs = shape->sub_block_size;
+    hipError_t e = launch_pool(shape->dtype, shape->head_dim, a, rows_of(shape), stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "pool_keys launch");
+}
+
+static int run_scores(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                      int32_t n_prev, int32_t *agn_state, int32_t *selected, float *scores_out, void *ws,
+                      hipStream_t stream) {
+    const bool scores_only = scores_out != nullptr;
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(pooled_k, 16);
+    REQUIRE_PTR(ws, kAlign);
+    if (scores_only) {
+        REQUIRE_PTR(scores_out, 4);
+    } else {
+        REQUIRE_PTR(evict, 4);
+        REQUIRE_PTR(selected, 4);
+        if (shape->ke > 0) REQUIRE_PTR(agn_state, 4);
+        if (n_prev < 0 || n_prev > shape->n_blocks)
+            return fail(NOSA_EINVAL, "n_blocks_prev %d must lie in [0, n_blocks=%d]", n_prev, shape->n_blocks);
+    }
+    const WsLayout L = ws_layout(shape);
+    const PartPlan pp = select_plan(shape);
+    SelectArgs a;
+    a.q = q;
+    a.kp = pooled_k;
+    a.ev = evict;
+    a.agn = agn_state;
+    a.sel = selected;
+    a.scores = scores_only ? scores_out : (float *)((char *)ws + L.scores);
+    a.cnt = (uint32_t *)((char *)ws + L.scnt);
+    a.Hq = shape->n_q_heads;
+    a.Hkv = shape->n_kv_heads;
+    a.G = group_of(shape);
+    a.n_blocks = shape->n_blocks;
+    a.n_blocks_max = shape->n_blocks_max;
+    a.kq = shape->kq;
+    a.ke = shape->ke;
+    a.n_prev = n_prev;
+    a.parts = pp.P;
+    a.blocks_per_part = pp.bpp;
+    a.scores_only = scores_only ? 1 : 0;
+    a.scores_stride = shape->n_blocks_max;
+    hipError_t e = launch_select(shape->dtype, shape->head_dim, spb_of(shape), a, rows_of(shape), stream);
+    return e == hipSuccess ? ok() : hip_fail(e, scores_only ? "block_scores launch" : "select launch");
+}
+
+int nosa_block_scores(const nosa_shape *shape, const void *q, const float *pooled_k, float *scores, void *ws,
+                      hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!scores) return fail(NOSA_EINVAL, "scores is NULL");
+    return run_scores(shape, q, pooled_k, nullptr, 0, nullptr, nullptr, scores, ws, stream);
+}
+
+int nosa_select(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, void *ws, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    return run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream);
+}
+
+int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
+                      int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
+                      const void *host_k, const void *host_v, void *cache_k, void *cache_v, hipStream_t compute,
+                      hipStream_t copy) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    const int k = shape->kq + shape->ke;
+    if (shape->cache_slots < k)
+        return fail(NOSA_ECAPACITY, "cache_slots %d is below the budget kq + ke = %d", shape->cache_slots, k);
+    if (shape->cache_slots > kMaxBlocks)
+        return fail(NOSA_EUNSUPPORTED, "cache_slots %d exceeds %d", shape->cache_slots, kMaxBlocks);
+    REQUIRE_PTR(selected, 4);
+    REQUIRE_PTR(slot_of_block, 4);
+    REQUIRE_PTR(block_of_slot, 4);
+    REQUIRE_PTR(block_table, 4);
+    REQUIRE_PTR(miss_cnt, 4);
+    REQUIRE_PTR(miss_list, 4);
+    REQUIRE_PTR(host_k, 16);
+    REQUIRE_PTR(host_v, 16);
+    REQUIRE_PTR(cache_k, 16);
+    REQUIRE_PTR(cache_v, 16);
+
+    void *dk = nullptr, *dv = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&dk, const_cast<void *>(host_k), 0);
+    if (e != hipSuccess || !dk) {
+        (void)hipGetLastError();
+        return fail(NOSA_EINVAL, "host_k is not pinned, device-mapped host memory (%s)", hipGetErrorString(e));
+    }
+    e = hipHostGetDevicePointer(&dv, const_cast<void *>(host_v), 0);
+    if (e != hipSuccess || !dv) {
+        (void)hipGetLastError();
+        return fail(NOSA_EINVAL, "host_v is not pinned, device-mapped host memory (%s)", hipGetErrorString(e));
+    }
+
+    const int R = rows_of(shape);
+    CacheArgs c;
+    c.sel = selected;
+    c.sob = slot_of_block;
+    c.bos = block_of_slot;
+    c.table = block_table;
+    c.mcnt = miss_cnt;
+    c.mlist = miss_list;
+    c.k = k;
+    c.C = shape->cache_slots;
+    c.nbmax = shape->n_blocks_max;
+    e = launch_cache_map(c, R, compute);
+    if (e != hipSuccess) return hip_fail(e, "cache_map launch");
+
+    GatherArgs g;
+    g.hk = (const unsigned char *)dk;
+    g.hv = (const unsigned char *)dv;
+    g.ck = (unsigned char *)cache_k;
+    g.cv = (unsigned char *)cache_v;
+    g.mcnt = miss_cnt;
+    g.mlist = miss_list;
+    g.k = k;
+    g.C = shape->cache_slots;
+    g.nbmax = shape->n_blocks_max;
+    g.block_bytes = (long long)shape->block_size * shape->head_dim * (long long)elem_bytes(shape);
+
+    if (copy == nullptr || copy == compute) {
+        e = launch_gather(g, R, compute);
+        return e == hipSuccess ? ok() : hip_fail(e, "gather launch");
+    }
+    DeviceEvents *ev = nullptr;
+    if ((rc = get_events(&ev)) != NOSA_OK) return rc;
+    if ((e = hipEventRecord(ev->mapped, compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(copy, ev->mapped, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if ((e = launch_gather(g, R, copy)) != hipSuccess) return hip_fail(e, "gather launch");
+    if ((e = hipEventRecord(ev->copied, copy)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(compute, ev->copied, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    return ok();
+}
+
+int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store, const void *v_store,
+                       int32_t store_blocks, const int32_t *block_table, float softmax_scale, void *out, void *ws,
+                       hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(k_store, 16);
+    REQUIRE_PTR(v_store, 16);
+    REQUIRE_PTR(block_table, 4);
+    REQUIRE_PTR(out, 16);
+    REQUIRE_PTR(ws, kAlign);
+    if (store_blocks < 1) return fail(NOSA_EINVAL, "store_blocks must be >= 1 (got %d)", store_blocks);
+    if (!(softmax_scale > 0.0f) || softmax_scale != softmax_scale)
+        return fail(NOSA_EINVAL, "softmax_scale must be a positive finite number");
+    const WsLayout L = ws_layout(shape);
+    const SplitPlan sp = decode_plan(shape);
+    DecodeArgs a;
+    a.q = q;
+    a.k = k_store;
+    a.v = v_store;
+    a.table = block_table;
+    a.out = out;
+    a.part = (float *)((char *)ws + L.part);
+    a.cnt = (uint32_t *)((char *)ws + L.dcnt);
+    a.Hq = shape->n_q_heads;
+    a.Hkv = shape->n_kv_heads;
+    a.k_sel = shape->kq + shape->ke;
+    a.store_blocks = store_blocks;
+    a.S = sp.S;
+    a.nbs = sp.nbs;
+    a.sl2 = softmax_scale * 1.4426950408889634f;
+    hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "sparse_decode launch");
+}
+
+}  // extern "C"

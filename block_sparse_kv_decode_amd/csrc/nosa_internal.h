@@ -1,0 +1,80 @@
+// nosa_internal.h -- launch descriptors shared by the host API (api.cpp) and the kernels.
+// Not part of the public ABI (that is include/nosa.h).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nosa {
+
+constexpr int kBlockTokens = 64;     // tokens per KV block (the selection / transfer unit)
+constexpr int kMaxBlocks = 16384;    // per-row block limit of the selection kernel's LDS
+
+struct PoolArgs {
+    const void *k;        // [R, nbmax, 64, d]
+    float *kp;            // [R, nbmax * spb, d]
+    int n_blocks_max;
+    int first_block;
+    int n_new;
+    int spb;              // sub-blocks per block
+    int sbs;              // tokens per sub-block
+};
+
+struct SelectArgs {
+    const void *q;        // [B, Hq, d]
+    const float *kp;      // [R, nbmax * spb, d]
+    const float *ev;      // [R, nbmax]
+    int32_t *agn;         // [R, ke]
+    int32_t *sel;         // [R, kq + ke]
+    float *scores;        // [R, scores_stride] global block scores (parts > 1, or scores-only mode)
+    uint32_t *cnt;        // [R] arrival counters (parts > 1)
+    int Hq, Hkv, G;
+    int n_blocks, n_blocks_max, kq, ke, n_prev;
+    int parts;            // workgroups per row
+    int blocks_per_part;
+    int scores_only;      // 1: stop after writing block scores
+    int scores_stride;
+};
+
+struct CacheArgs {
+    const int32_t *sel;   // [R, k]
+    int32_t *sob;         // [R, nbmax]
+    int32_t *bos;         // [R, C]
+    int32_t *table;       // [R, k]
+    int32_t *mcnt;        // [R]
+    int32_t *mlist;       // [R, k, 2]
+    int k, C, nbmax;
+};
+
+struct GatherArgs {
+    const unsigned char *hk, *hv;   // device-mapped pinned host pools [R, nbmax, block_bytes]
+    unsigned char *ck, *cv;         // cache [R, C, block_bytes]
+    const int32_t *mcnt;
+    const int32_t *mlist;
+    int k, C, nbmax;
+    long long block_bytes;
+};
+
+struct DecodeArgs {
+    const void *q;        // [B, Hq, d]
+    const void *k, *v;    // [R, store_blocks, 64, d]
+    const int32_t *table; // [R, k_sel]
+    void *out;            // [B, Hq, d]
+    float *part;          // [R, S, G, d + 2] split partials (S > 1)
+    uint32_t *cnt;        // [R] arrival counters (S > 1)
+    int Hq, Hkv, k_sel, store_blocks;
+    int S;                // splits per row
+    int nbs;              // blocks per split
+    float sl2;            // softmax scale * log2(e)
+};
+
+// Each launcher returns hipSuccess or the error of the launch.
+hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_t st);
+hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, hipStream_t st);
+size_t select_lds_bytes(int n_blocks);
+hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
+hipError_t launch_gather(const GatherArgs &a, int rows, hipStream_t st);
+hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st);
+
+}  // namespace nosa

@@ -1,0 +1,196 @@
+/*
+ * nosa.h -- C ABI of the NOSA decode-step hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method is NOSA, "NOSA: Native and Offloadable Sparse Attention" (arXiv 2510.13602),
+ * as described on
+ *   [P1] the paperlayer.ai structured summary of the paper (sections as numbered there), and
+ *   [P4] the gist.science explainer, part "Technical summary", Method sections 1 and 2.
+ *
+ * One decode step of one attention layer, per sequence b and KV head g (a "row"):
+ *   1. score every visible KV block against the query        -> nosa_select    ([P1] §2.1, §3.1)
+ *   2. pick k = kq + ke blocks: ke query-agnostic blocks under strict eviction, then the
+ *      kq best query-aware blocks among the rest              -> nosa_select    ([P1] §2.1, App. A, App. E)
+ *   3. (offloaded KV only) hit/miss check against the GPU block cache, replacement map and
+ *      host-to-GPU copy of the missed blocks                  -> nosa_cache_update ([P1] §4, App. A)
+ *   4. GQA attention over the tokens of the selected blocks  -> nosa_sparse_decode ([P1] App. A)
+ * Pooled keys (sub-block means) are state kept next to the KV cache -> nosa_pool_keys ([P1] §3.1).
+ *
+ * Conventions for every entry point
+ *   - All buffers are owned by the caller.  Device pointers point to GPU memory of the current
+ *     HIP device; host pools are pinned (page-locked, device-mapped) host memory.  The library
+ *     allocates no memory.
+ *   - Calls only enqueue work on the given stream(s) and never synchronise the host.
+ *   - Shapes, pointers and alignment are validated on the host before any HIP call; a rejected
+ *     call returns a negative nosa_status, launches nothing and leaves every buffer untouched.
+ *     nosa_last_error() returns a message for the last failure of the calling thread.
+ *   - Layouts are dense, row-major, in the order written: [B, Hkv, ...] rows are indexed
+ *     r = b * n_kv_heads + g, and query head h belongs to KV head h / (n_q_heads / n_kv_heads).
+ *   - Element type of q, K, V and the output: NOSA_BF16 (bfloat16) or NOSA_F32.  Pooled keys,
+ *     eviction scores and block scores are float32.  Accumulation is float32 everywhere.
+ *   - Supported set: head_dim 64 or 128; block_size 64; sub_block_size 8, 16, 32 or 64;
+ *     n_q_heads / n_kv_heads in {1, 2, 4, 8}; 1 <= kq + ke <= n_blocks <= n_blocks_max <= 16384;
+ *     cache_slots >= kq + ke (for nosa_cache_update).  Anything else returns NOSA_EUNSUPPORTED
+ *     or NOSA_EINVAL.
+ *   - Workspace: nosa_workspace_bytes() bytes of device memory, 256-byte aligned, zero-filled once
+ *     by the caller before its first use.  Each call leaves the workspace's internal counters at
+ *     zero again, so it can be reused without clearing.  Calls that share a workspace must be
+ *     ordered (same stream, or synchronised); concurrent calls on one workspace race.
+ */
+#ifndef NOSA_H
+#define NOSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NOSA_OK = 0,
+    NOSA_EINVAL = -1,        /* malformed argument: null/misaligned pointer, inconsistent sizes */
+    NOSA_EUNSUPPORTED = -2,  /* well-formed but outside the supported set listed above */
+    NOSA_ECAPACITY = -3,     /* workspace or cache too small for the request */
+    NOSA_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+} nosa_status;
+
+typedef enum { NOSA_F32 = 0, NOSA_BF16 = 1 } nosa_dtype;
+
+/* Sizes of one decode step of one attention layer. */
+typedef struct {
+    int32_t batch;           /* B: sequences decoded together */
+    int32_t n_q_heads;       /* Hq: query heads */
+    int32_t n_kv_heads;      /* Hkv: KV heads (Hq % Hkv == 0; G = Hq / Hkv heads share one KV head) */
+    int32_t head_dim;        /* d */
+    int32_t block_size;      /* tokens per KV block: the unit of selection and transfer (64) */
+    int32_t sub_block_size;  /* tokens per mean-pooled sub-block (divides block_size) */
+    int32_t n_blocks;        /* blocks visible at this step (whole blocks of the context) */
+    int32_t n_blocks_max;    /* blocks allocated per row in K/V stores, pooled keys, eviction scores */
+    int32_t kq;              /* query-aware budget, blocks */
+    int32_t ke;              /* query-agnostic budget, blocks */
+    int32_t cache_slots;     /* C: GPU cache slots per row (nosa_cache_update only; else ignored) */
+    int32_t dtype;           /* nosa_dtype of q, K, V, output */
+    int32_t decode_splits;   /* split-K partitions per row in nosa_sparse_decode; 0 = automatic */
+    int32_t select_parts;    /* workgroups that score one row in nosa_select; 0 = automatic */
+} nosa_shape;
+
+/* Message for the last failed call on this thread ("" if none).  Never NULL. */
+const char *nosa_last_error(void);
+
+/* Library build identifier (compile target and version string). */
+const char *nosa_version(void);
+
+/* Device workspace bytes needed by nosa_select / nosa_block_scores / nosa_sparse_decode for this
+ * shape (the same workspace serves all three).  Returns 0 if the shape is invalid (see
+ * nosa_last_error). */
+size_t nosa_workspace_bytes(const nosa_shape *shape);
+
+/*
+ * Sub-block mean pooling of keys ([P1] §3.1 and [P4] Method 1: the first pooling stage averages
+ * the keys of each sub-block).
+ *   k        : device, [B, Hkv, n_blocks_max, block_size, d], dtype   (16-byte aligned)
+ *   pooled_k : device, [B, Hkv, n_blocks_max * spb, d] float32, spb = block_size / sub_block_size
+ * For blocks first_block .. first_block + n_new - 1 (all rows):
+ *   pooled_k[r][j][c] = (sum of k over the sub_block_size tokens of sub-block j) / sub_block_size,
+ * summed in float32 in token order.  Other entries are untouched.  Requires
+ * 0 <= first_block, first_block + n_new <= n_blocks_max, n_new >= 0.
+ */
+int nosa_pool_keys(const nosa_shape *shape, const void *k, int32_t first_block, int32_t n_new,
+                   float *pooled_k, hipStream_t stream);
+
+/*
+ * Query-aware block scores only (the scoring half of nosa_select, exposed for inspection;
+ * [P1] §2.1 and §3.1: query-key similarity on mean-pooled sub-blocks, max-pooled per block).
+ * For row r = (b, g) and visible block i < n_blocks:
+ *   u[j]        = sum over the G query heads h of group g of  q[b][h] . pooled_k[r][j]
+ *   scores[r][i] = max of u[j] over the block's sub-blocks j = i*spb .. i*spb + spb - 1
+ * (computed as (sum_h q[b][h]) . pooled_k[r][j] in float32; the two agree up to rounding).
+ *   q       : device, [B, Hq, d], dtype                 pooled_k : as in nosa_pool_keys
+ *   scores  : device, [B, Hkv, n_blocks_max] float32, entries >= n_blocks untouched
+ *   ws      : device workspace (see above)
+ */
+int nosa_block_scores(const nosa_shape *shape, const void *q, const float *pooled_k, float *scores,
+                      void *ws, hipStream_t stream);
+
+/*
+ * Block selection for one decode step ([P1] §2.1, §3.1, App. A, App. E; [P4] Method 1).
+ * Per row, with the block scores s of nosa_block_scores and the fixed per-block eviction scores e:
+ *   Query-agnostic subset Gamma_e (ke blocks, highest e first):
+ *     n_blocks_prev == 0 : chosen among all visible blocks [0, n_blocks)  (first step).
+ *     n_blocks_prev  > 0 : chosen among Gamma_e of the previous step (agn_state on entry) and the
+ *                          blocks [n_blocks_prev, n_blocks) that became visible since then.  A block
+ *                          once left out of Gamma_e never re-enters it (strict eviction), so
+ *                          consecutive selections share at least ke - (admitted arrivals) blocks.
+ *   Query-aware subset Gamma_q: the kq visible blocks outside Gamma_e with the highest s.
+ *   Ties on e or s go to the lower block id.  The selection is Gamma_e U Gamma_q, k = kq + ke
+ *   distinct blocks, written in ascending block id.
+ *   q           : device, [B, Hq, d], dtype
+ *   pooled_k    : device, [B, Hkv, n_blocks_max * spb, d] float32 (nosa_pool_keys)
+ *   evict       : device, [B, Hkv, n_blocks_max] float32, first n_blocks used; finite values
+ *   n_blocks_prev : 0, or the n_blocks of the previous step for this agn_state (<= n_blocks)
+ *   agn_state   : device, [B, Hkv, ke] int32, in (when n_blocks_prev > 0) / out: Gamma_e ascending.
+ *                 Entries outside [0, n_blocks_prev) on entry are ignored.
+ *   selected    : device, [B, Hkv, kq + ke] int32, out: block ids ascending
+ *   ws          : device workspace
+ * Non-finite q, pooled keys or eviction scores are outside the contract.
+ */
+int nosa_select(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, void *ws,
+                hipStream_t stream);
+
+/*
+ * Cache hit/miss check, replacement map and host-to-GPU block transfer for offloaded KV
+ * ([P1] §4: set difference of old and new selections into a replacement map, only blocks unused
+ * at this step are swapped out, fine-grained block transfers from host memory; [P1] App. A).
+ * Per row, against a cache of C = cache_slots slots:
+ *   hits   = selected blocks already resident (slot_of_block[blk] >= 0);
+ *   misses = the other selected blocks, in ascending block id;
+ *   free   = slots that are empty or hold a block not selected now, in ascending slot index;
+ *   the i-th miss takes the i-th free slot (its previous block, if any, becomes non-resident).
+ *   selected      : device, [B, Hkv, k] int32 ascending (nosa_select output)
+ *   slot_of_block : device, [B, Hkv, n_blocks_max] int32, in/out, -1 = not resident
+ *   block_of_slot : device, [B, Hkv, C] int32, in/out, -1 = empty (both maps start all -1)
+ *   block_table   : device, [B, Hkv, k] int32, out: the slot holding selected[i]
+ *   miss_cnt      : device, [B, Hkv] int32, out
+ *   miss_list     : device, [B, Hkv, k, 2] int32, out: (block, slot) of the first miss_cnt misses
+ *   host_k/host_v : pinned host memory, [B, Hkv, n_blocks_max, block_size, d], dtype; the library
+ *                   reads it through its device mapping (hipHostGetDevicePointer)
+ *   cache_k/cache_v : device, [B, Hkv, C, block_size, d], dtype; missed blocks are copied in
+ *   compute       : stream of the map update; copy : stream of the block transfer (may equal
+ *                   compute or be NULL = compute).  On return, work later enqueued on `compute`
+ *                   is ordered after the transfer.
+ * Selected ids outside [0, n_blocks_max) are skipped.  Maps that are not mutual inverses are
+ * outside the contract.
+ */
+int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
+                      int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt,
+                      int32_t *miss_list, const void *host_k, const void *host_v, void *cache_k,
+                      void *cache_v, hipStream_t compute, hipStream_t copy);
+
+/*
+ * GQA sparse attention of one decode query per head over the selected blocks ([P1] App. A;
+ * the pages give no formula: standard scaled dot-product attention restricted to the tokens of
+ * the selected blocks).  For query head h of sequence b, KV head g = h / G, row r = (b, g):
+ *   T      = the block_size tokens of each store block block_table[r][0 .. k-1]
+ *   z_t    = softmax_scale * q[b][h] . k_store[r][blk][t]
+ *   out[b][h] = sum_t softmax(z)_t * v_store[r][blk][t]
+ * computed as split-K flash decoding (online softmax, float32 accumulation).
+ *   q        : device, [B, Hq, d], dtype
+ *   k_store, v_store : device, [B, Hkv, store_blocks, block_size, d], dtype -- the resident KV
+ *              (store_blocks = n_blocks_max, table = selected) or the GPU cache
+ *              (store_blocks = cache_slots, table = block_table of nosa_cache_update)
+ *   block_table : device, [B, Hkv, k] int32 with k = kq + ke; entries outside [0, store_blocks)
+ *              are skipped
+ *   out      : device, [B, Hq, d], dtype
+ *   ws       : device workspace
+ */
+int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store,
+                       const void *v_store, int32_t store_blocks, const int32_t *block_table,
+                       float softmax_scale, void *out, void *ws, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NOSA_H */

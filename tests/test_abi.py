@@ -1,0 +1,116 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry point the header
+declares, and rejects malformed calls on the host before any HIP call."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_kv_decode_amd as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nosa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nosa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert set(names) == set(N.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (nosa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(N.lib, n)
+    # binding exposes the same names
+    for n in names:
+        assert callable(getattr(N, n))
+
+
+def _good(**kw):
+    base = dict(batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, n_blocks=256, kq=32, ke=32, cache_slots=64)
+    base.update(kw)
+    return N.make_shape(**base)
+
+
+def test_workspace_bytes():
+    s = _good()
+    n = N.nosa_workspace_bytes(s)
+    assert n > 0 and n % 256 == 0
+    # the block score buffer alone needs rows * n_blocks_max floats
+    assert n >= 16 * 8 * 256 * 4
+    assert N.nosa_workspace_bytes(_good(decode_splits=8)) > N.nosa_workspace_bytes(_good(decode_splits=1))
+
+
+BAD = [
+    (dict(n_q_heads=30), N.NOSA_EINVAL),                    # Hq not a multiple of Hkv
+    (dict(n_q_heads=48, n_kv_heads=3), N.NOSA_EUNSUPPORTED),  # G = 16
+    (dict(head_dim=96), N.NOSA_EUNSUPPORTED),
+    (dict(block_size=32), N.NOSA_EUNSUPPORTED),
+    (dict(sub_block_size=24), N.NOSA_EUNSUPPORTED),
+    (dict(dtype=7), N.NOSA_EUNSUPPORTED),
+    (dict(kq=200, ke=100), N.NOSA_EINVAL),                   # budget above visible blocks
+    (dict(kq=0, ke=0), N.NOSA_EINVAL),
+    (dict(kq=-1), N.NOSA_EINVAL),
+    (dict(n_blocks=300, n_blocks_max=256), N.NOSA_EINVAL),
+    (dict(n_blocks=0), N.NOSA_EINVAL),
+    (dict(n_blocks_max=20000, n_blocks=256), N.NOSA_EUNSUPPORTED),
+    (dict(batch=0), N.NOSA_EINVAL),
+    (dict(decode_splits=-2), N.NOSA_EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_invalid_shapes_rejected_on_host(kw, code):
+    s = _good(**kw)
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_select(s, 16, 16, 16, 0, 16, 16, 256, stream=0)
+    assert ei.value.code == code
+    assert N.nosa_last_error() != ""
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, 0.1, 16, 256, stream=0)
+    assert ei.value.code == code
+    assert N.lib.nosa_workspace_bytes(s) == 0
+
+
+def test_invalid_pointers_rejected_on_host():
+    s = _good()
+    cases = [
+        lambda: N.nosa_select(s, None, 16, 16, 0, 16, 16, 256, stream=0),
+        lambda: N.nosa_select(s, 8, 16, 16, 0, 16, 16, 256, stream=0),          # q misaligned
+        lambda: N.nosa_select(s, 16, 16, 16, 0, 16, 16, 128, stream=0),         # ws misaligned
+        lambda: N.nosa_select(s, 16, 16, 16, 300, 16, 16, 256, stream=0),       # n_blocks_prev > n_blocks
+        lambda: N.nosa_select(s, 16, 16, 16, -1, 16, 16, 256, stream=0),
+        lambda: N.nosa_sparse_decode(s, 16, 16, 16, 0, 16, 0.1, 16, 256, stream=0),    # store_blocks 0
+        lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, -1.0, 16, 256, stream=0), # bad scale
+        lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, float("nan"), 16, 256, stream=0),
+        lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, None, 0.1, 16, 256, stream=0),
+        lambda: N.nosa_pool_keys(s, 16, 250, 10, 16, stream=0),                 # past n_blocks_max
+        lambda: N.nosa_pool_keys(s, 16, -1, 1, 16, stream=0),
+        lambda: N.nosa_block_scores(s, 16, 16, None, 256, stream=0),
+    ]
+    for f in cases:
+        with pytest.raises(N.NosaError) as ei:
+            f()
+        assert ei.value.code == N.NOSA_EINVAL, N.nosa_last_error()
+
+
+def test_cache_update_rejects_small_cache_and_null():
+    s = _good(cache_slots=10)
+    args = [16] * 10
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_cache_update(s, *args, compute=0, copy=0)
+    assert ei.value.code == N.NOSA_ECAPACITY
+    s = _good()
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_cache_update(s, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, compute=0, copy=0)
+    assert ei.value.code == N.NOSA_EINVAL
+
+
+def test_pool_keys_zero_blocks_is_a_noop():
+    N.nosa_pool_keys(_good(), 16, 5, 0, 16, stream=0)   # validates, launches nothing

@@ -1,0 +1,115 @@
+"""Full-size parity on the configured workloads, in the launch configuration the benchmark
+times (automatic splits and parts): C2 (B16, 16K ctx), C3 (B64, 4K ctx), C5 (B4, 128K ctx)
+end to end against the oracle element by element, and the C4 offload loop (128 steps) with
+per-step invariants and oracle checks on sampled steps."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import block_sparse_kv_decode_amd as N  # noqa: E402
+from nosa_inputs import WORKLOADS, generate, visible_blocks  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from tests import gpuhelp as H  # noqa: E402
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C5"])
+def test_resident_config_end_to_end(cfg):
+    w = WORKLOADS[cfg]
+    x = generate(w)
+    shape = H.shape_of(w)
+    q_dev, k_dev, v_dev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"])
+    kp = H.gpu_pool(shape, k_dev)
+    ws = N.workspace(shape)
+    sel, agn = H.gpu_select(shape, q_dev, kp, H.dev(x["evict"]), ws)
+    out = H.gpu_decode(shape, q_dev, k_dev, v_dev, w.nbmax, sel, ws)
+    torch.cuda.synchronize()
+    kp_ref = O.pool_keys(x["k"], 32)
+    np.testing.assert_allclose(H.host(kp).reshape(kp_ref.shape), kp_ref, rtol=1e-6, atol=1e-6)
+    s_ref = O.block_scores(x["q"], kp_ref, w.n_blocks, 2)
+    ties = H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke)
+    sel_h = H.host(sel).reshape(w.batch, w.n_kv_heads, w.k)
+    ref = O.attention(x["q"], x["k"], x["v"], sel_h)
+    stats = H.check_attention(H.host(out), ref, w.dtype, cfg)
+    print(cfg, "tie rows", ties, stats)
+    # the same step again: bitwise identical
+    sel2, _ = H.gpu_select(shape, q_dev, kp, H.dev(x["evict"]), ws)
+    out2 = H.gpu_decode(shape, q_dev, k_dev, v_dev, w.nbmax, sel2, ws)
+    assert torch.equal(sel, sel2) and torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_c4_offload_loop():
+    w = WORKLOADS["C4"]
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    R, k, C = w.rows, w.k, w.cache_slots
+    hk, hv = H.pinned(x["k"]), H.pinned(x["v"])
+    kp = H.gpu_pool(shape0, H.dev(x["k"]))          # pooled keys: setup, from a device copy
+    torch.cuda.synchronize()
+    ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    cv = torch.zeros_like(ck)
+    sob = torch.full((R, w.nbmax), -1, dtype=torch.int32, device="cuda")
+    bos = torch.full((R, C), -1, dtype=torch.int32, device="cuda")
+    table = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    mcnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    mlist = torch.empty((R, k, 2), dtype=torch.int32, device="cuda")
+    ws = N.workspace(shape0)
+    ev_dev = H.dev(x["evict"])
+    q_all = H.dev(x["q_steps"])
+    copy_stream = torch.cuda.Stream()
+    kp_ref = None
+    sampled = {0, 1, 63, 64, 65, w.steps - 1}
+    agn = None
+    prev_sel = None
+    n_prev = 0
+    gammas, hits = [], []
+    for t in range(w.steps):
+        n = visible_blocks(w, t)
+        shape = shape0.copy(n_blocks=n)
+        if t in sampled:
+            torch.cuda.synchronize()
+            snap = {"agn": None if agn is None else H.host(agn).copy(), "sob": H.host(sob).copy(),
+                    "bos": H.host(bos).copy()}
+        q_t = q_all[t]
+        sel, agn = H.gpu_select(shape, q_t, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
+        N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, copy=copy_stream)
+        out = H.gpu_decode(shape, q_t, ck, cv, C, table, ws)
+        torch.cuda.synchronize()
+        sel_h = H.host(sel)
+        mc = H.host(mcnt)
+        assert np.all(np.diff(sel_h, axis=1) > 0) and sel_h.min() >= 0 and sel_h.max() < n
+        if prev_sel is not None:
+            gam = O.locality(prev_sel, sel_h, w.nbmax)
+            admitted = np.array([len(set(H.host(agn)[r].tolist()) & set(range(n_prev, n))) for r in range(R)])
+            assert np.all(gam >= (w.ke - admitted) / k - 1e-12)
+            # cache = budget: the cache after step t-1 holds exactly Gamma(t-1), so hits = k * gamma
+            assert np.array_equal(k - mc, np.rint(k * gam).astype(np.int32))
+            gammas.append(gam)
+        hits.append(k - mc)
+        if t in sampled:
+            if kp_ref is None:
+                kp_ref = O.pool_keys(x["k"], 32)
+            s_ref = O.block_scores(x["q_steps"][t], kp_ref[:, :, :2 * n], n, 2)
+            H.check_selection(sel_h, H.host(agn), s_ref, x["evict"], w.kq, w.ke, n_prev,
+                              None if snap["agn"] is None else snap["agn"].reshape(w.batch, w.n_kv_heads, w.ke))
+            sob_ref, bos_ref = snap["sob"], snap["bos"]
+            tab_ref, mc_ref, ml_ref = O.cache_step(sel_h, sob_ref, bos_ref)
+            assert np.array_equal(H.host(sob), sob_ref) and np.array_equal(H.host(bos), bos_ref)
+            assert np.array_equal(H.host(table), tab_ref) and np.array_equal(mc, mc_ref)
+            ref = O.attention(x["q_steps"][t], x["k"], x["v"], sel_h.reshape(w.batch, w.n_kv_heads, k))
+            H.check_attention(H.host(out), ref, "bf16", "C4 step %d" % t)
+            # every cache slot holds the bytes of the block the map says it holds
+            ckh, cvh, bosh = H.host(ck), H.host(cv), H.host(bos)
+            for r in range(0, R, 17):
+                b, g = divmod(r, w.n_kv_heads)
+                for s_, blk in enumerate(bosh[r]):
+                    if blk >= 0:
+                        assert np.array_equal(ckh[b, g, s_], x["k"][b, g, blk])
+                        assert np.array_equal(cvh[b, g, s_], x["v"][b, g, blk])
+        prev_sel = sel_h
+        n_prev = n
+    g = np.concatenate(gammas)
+    print("C4 gamma min %.3f mean %.3f; hit rate (warm) %.3f" % (g.min(), g.mean(), np.mean(hits[1:]) / k))
+    assert g.min() >= w.ke / k - 1e-12

@@ -1,0 +1,258 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on reduced shapes that span
+several workgroups, splits and parts with ragged tails, plus the edge cases of the method."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import block_sparse_kv_decode_amd as N  # noqa: E402
+from nosa_inputs import generate, small_workload  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from tests import gpuhelp as H  # noqa: E402
+
+# name -> (workload kwargs, sub_block_size)
+CASES = {
+    "g4_d128_bf16_ragged": (dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=37, n_blocks_max=41,
+                                 kq=5, ke=7, seed=21), 32),
+    "g2_d64_bf16_sbs16": (dict(batch=3, n_q_heads=6, n_kv_heads=3, head_dim=64, n_blocks=50, kq=9, ke=4, seed=22), 16),
+    "g8_d128_bf16_sbs64": (dict(batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128, n_blocks=33, kq=3, ke=13,
+                                seed=23), 64),
+    "g1_d64_f32_ke_only": (dict(batch=2, n_q_heads=2, n_kv_heads=2, head_dim=64, n_blocks=20, kq=0, ke=6,
+                                dtype="f32", seed=24), 8),
+    "g4_d128_bf16_kq_only": (dict(batch=2, n_q_heads=4, n_kv_heads=1, head_dim=128, n_blocks=70, kq=20, ke=0,
+                                  seed=25), 32),
+    "g2_d64_f32_all_blocks": (dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=64, n_blocks=12, kq=5, ke=7,
+                                   dtype="f32", seed=26), 32),
+    "g4_d64_f32": (dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, n_blocks=45, kq=6, ke=6, dtype="f32",
+                        seed=27), 32),
+    "g2_d128_f32": (dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, n_blocks=19, kq=4, ke=4, dtype="f32",
+                         seed=28), 32),
+}
+
+
+def _setup(name):
+    kw, sbs = CASES[name]
+    w = small_workload(name, **kw)
+    x = generate(w)
+    return w, x, sbs
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_pool_keys(name):
+    w, x, sbs = _setup(name)
+    shape = H.shape_of(w, sub_block_size=sbs)
+    kp = H.host(H.gpu_pool(shape, H.dev(x["k"])))
+    ref = O.pool_keys(x["k"], sbs).reshape(kp.shape)
+    np.testing.assert_allclose(kp, ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("parts", [0, 1, 3, 7])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_block_scores(name, parts):
+    w, x, sbs = _setup(name)
+    shape = H.shape_of(w, sub_block_size=sbs, select_parts=parts)
+    spb = 64 // sbs
+    kp_dev = H.gpu_pool(shape, H.dev(x["k"]))
+    ws = N.workspace(shape)
+    scores = torch.full((w.rows, w.nbmax), float("nan"), dtype=torch.float32, device="cuda")
+    N.nosa_block_scores(shape, H.dev(x["q"]), kp_dev, scores, ws)
+    s = H.host(scores)
+    ref = O.block_scores(x["q"], O.pool_keys(x["k"], sbs), w.n_blocks, spb).reshape(w.rows, -1)
+    assert np.all(np.isnan(s[:, w.n_blocks:]))          # entries past n_blocks untouched
+    scale = np.abs(ref).max(axis=1, keepdims=True)
+    assert np.all(np.abs(s[:, :w.n_blocks] - ref) <= 1e-5 * scale + 1e-6)
+
+
+@pytest.mark.parametrize("parts", [0, 1, 4])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_select(name, parts):
+    w, x, sbs = _setup(name)
+    shape = H.shape_of(w, sub_block_size=sbs, select_parts=parts)
+    q_dev = H.dev(x["q"])
+    kp_dev = H.gpu_pool(shape, H.dev(x["k"]))
+    ws = N.workspace(shape)
+    sel, agn = H.gpu_select(shape, q_dev, kp_dev, H.dev(x["evict"]), ws)
+    s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], sbs), w.n_blocks, 64 // sbs)
+    H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"][:, :, :w.n_blocks], w.kq, w.ke)
+    # repeat: bitwise identical (deterministic, workspace counters reset)
+    sel2, agn2 = H.gpu_select(shape, q_dev, kp_dev, H.dev(x["evict"]), ws)
+    assert torch.equal(sel, sel2) and torch.equal(agn, agn2)
+
+
+def test_select_ties_lowest_ids():
+    # All-zero pooled keys: every block score is 0 -> Gamma_q takes the lowest ids outside Gamma_e.
+    # Equal eviction scores -> Gamma_e takes the lowest ids.
+    w = small_workload("ties", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=40, kq=6, ke=5, seed=30)
+    x = generate(w)
+    shape = H.shape_of(w)
+    kp = torch.zeros((w.rows, w.nbmax * 2, 128), dtype=torch.float32, device="cuda")
+    ev = torch.full((w.batch, w.n_kv_heads, w.nbmax), 0.5, dtype=torch.float32, device="cuda")
+    sel, agn = H.gpu_select(shape, H.dev(x["q"]), kp, ev, N.workspace(shape))
+    assert H.host(agn).tolist() == [[0, 1, 2, 3, 4]] * w.rows
+    assert H.host(sel).tolist() == [list(range(11))] * w.rows
+
+
+def test_select_planted_blocks():
+    # Blocks whose keys carry an offset along the summed group query must be chosen by the
+    # query-aware part whatever their eviction score.
+    w = small_workload("planted", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=60, kq=3, ke=4,
+                       seed=31, block_offset_sigma=0.0, dtype="f32")
+    x = generate(w)
+    k = x["k"].copy()
+    planted = {(0, 0): [5, 17, 44], (0, 1): [0, 59, 30], (1, 0): [12, 13, 14], (1, 1): [58, 2, 40]}
+    for (b, g), blks in planted.items():
+        qs = x["q"][b, g * 4:(g + 1) * 4].sum(axis=0)
+        for j, blk in enumerate(blks):
+            k[b, g, blk] += (4.0 + j) * qs / np.linalg.norm(qs)
+    ev = np.zeros_like(x["evict"])
+    for (b, g), blks in planted.items():
+        ev[b, g] = np.linspace(0, 1, w.nbmax, dtype=np.float32)  # Gamma_e = last 4 blocks
+        ev[b, g, blks] = -1.0
+    shape = H.shape_of(w)
+    kp = H.gpu_pool(shape, H.dev(k))
+    sel, agn = H.gpu_select(shape, H.dev(x["q"]), kp, H.dev(ev), N.workspace(shape))
+    sel = H.host(sel).reshape(2, 2, 7)
+    for (b, g), blks in planted.items():
+        assert set(blks) <= set(sel[b, g].tolist())
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 5])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_sparse_decode(name, splits):
+    w, x, sbs = _setup(name)
+    shape = H.shape_of(w, sub_block_size=sbs, decode_splits=splits)
+    rng = np.random.default_rng(w.seed)
+    k = w.k
+    table = np.stack([np.sort(rng.choice(w.n_blocks, k, replace=False)) for _ in range(w.rows)]).astype(np.int32)
+    table = table.reshape(w.batch, w.n_kv_heads, k)
+    out = H.gpu_decode(shape, H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), w.nbmax, H.dev(table), N.workspace(shape))
+    ref = O.attention(x["q"], x["k"], x["v"], table)
+    H.check_attention(H.host(out), ref, w.dtype, name)
+
+
+def test_sparse_decode_store_layout_and_order_invariance():
+    # Table in a shuffled order over a store with extra blocks gives the same attention (up to
+    # rounding): the softmax runs over the set of selected tokens.
+    w = small_workload("perm", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=30, n_blocks_max=35,
+                       kq=6, ke=6, seed=32)
+    x = generate(w)
+    shape = H.shape_of(w)
+    rng = np.random.default_rng(3)
+    table = np.stack([rng.choice(w.nbmax, 12, replace=False) for _ in range(w.rows)]).astype(np.int32)
+    table = table.reshape(2, 2, 12)
+    ws = N.workspace(shape)
+    o1 = H.host(H.gpu_decode(shape, H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), w.nbmax, H.dev(table), ws))
+    ref = O.attention(x["q"], x["k"], x["v"], table)
+    H.check_attention(o1, ref, "bf16", "shuffled table")
+
+
+def test_sparse_decode_skips_out_of_range_ids():
+    w = small_workload("skip", batch=1, n_q_heads=4, n_kv_heads=1, head_dim=128, n_blocks=10, kq=2, ke=2, seed=33)
+    x = generate(w)
+    shape = H.shape_of(w, decode_splits=1)
+    table = np.array([[[1, 4, -1, 7]]], np.int32)
+    out = H.host(H.gpu_decode(shape, H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), w.nbmax, H.dev(table),
+                              N.workspace(shape)))
+    ref = O.attention(x["q"], x["k"], x["v"], np.array([[[1, 4, 7]]], np.int32))
+    H.check_attention(out, ref, "bf16", "skip")
+
+
+def test_multistep_select_with_arrivals():
+    # Strict eviction across steps: blocks arrive one by one; Gamma_e on the GPU follows the
+    # oracle exactly, and the selection matches within the tie band.
+    w = small_workload("multi", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=30, n_blocks_max=46,
+                       kq=5, ke=6, seed=34)
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    kp_dev = H.gpu_pool(shape0, H.dev(x["k"]))
+    ev_dev = H.dev(x["evict"])
+    ws = N.workspace(shape0)
+    kp_ref = O.pool_keys(x["k"], 32)
+    rng = np.random.default_rng(5)
+    qf = x["q"]
+    n, agn_dev, agn_ref = 30, None, None
+    for t in range(12):
+        n_prev = 0 if t == 0 else n
+        if t > 0:
+            n = min(w.nbmax, n + int(rng.integers(0, 3)))
+        q_t = H.dev(qf)
+        shape = shape0.copy(n_blocks=n)
+        sel, agn_dev = H.gpu_select(shape, q_t, kp_dev, ev_dev, ws, n_prev=n_prev, agn=agn_dev)
+        s_ref = O.block_scores(qf, kp_ref[:, :, :n * 2], n, 2)
+        H.check_selection(H.host(sel), H.host(agn_dev), s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
+        _, agn_ref, _ = O.select(s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
+        qf = (H.as_f64(qf) + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32)
+        from nosa_inputs import f32_to_bf16_bits
+        qf = f32_to_bf16_bits(qf)
+
+
+@pytest.mark.parametrize("side_stream", [False, True])
+def test_cache_update_and_offload_decode(side_stream):
+    # Offload loop at reduced size: GPU maps, tables, miss lists and cache bytes follow the oracle's
+    # cache simulation exactly; attention from the cache matches the oracle.
+    w = small_workload("offload", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=40, n_blocks_max=44,
+                       kq=6, ke=6, seed=35, cache_slots=15)
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    R, k, C = w.rows, w.k, w.cache_slots
+    hk, hv = H.pinned(x["k"]), H.pinned(x["v"])
+    ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, 128), dtype=torch.bfloat16, device="cuda")
+    cv = torch.zeros_like(ck)
+    sob = torch.full((R, w.nbmax), -1, dtype=torch.int32, device="cuda")
+    bos = torch.full((R, C), -1, dtype=torch.int32, device="cuda")
+    table = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    mcnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    mlist = torch.empty((R, k, 2), dtype=torch.int32, device="cuda")
+    sob_ref = np.full((R, w.nbmax), -1, np.int32)
+    bos_ref = np.full((R, C), -1, np.int32)
+    ck_ref = np.zeros((w.batch, w.n_kv_heads, C, 64, 128), np.uint16)
+    cv_ref = np.zeros_like(ck_ref)
+    kp_dev = H.gpu_pool(shape0, H.dev(x["k"]))
+    ws = N.workspace(shape0)
+    ev_dev = H.dev(x["evict"])
+    copy_stream = torch.cuda.Stream() if side_stream else None
+    rng = np.random.default_rng(6)
+    qf = x["q"]
+    n, agn = 40, None
+    from nosa_inputs import f32_to_bf16_bits
+    for t in range(10):
+        n_prev = 0 if t == 0 else n
+        if t in (3, 6, 7):
+            n += 1
+        shape = shape0.copy(n_blocks=n)
+        q_dev = H.dev(qf)
+        sel, agn = H.gpu_select(shape, q_dev, kp_dev, ev_dev, ws, n_prev=n_prev, agn=agn)
+        N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, copy=copy_stream)
+        out = H.gpu_decode(shape, q_dev, ck, cv, C, table, ws)
+        torch.cuda.synchronize()
+        sel_h = H.host(sel)
+        tab_ref, mc_ref, ml_ref = O.cache_step(sel_h, sob_ref, bos_ref)
+        assert np.array_equal(H.host(sob), sob_ref) and np.array_equal(H.host(bos), bos_ref)
+        assert np.array_equal(H.host(table), tab_ref) and np.array_equal(H.host(mcnt), mc_ref)
+        ml = H.host(mlist)
+        for r in range(R):
+            assert np.array_equal(ml[r, :mc_ref[r]], ml_ref[r, :mc_ref[r]])
+        O.gather(mc_ref.reshape(w.batch, w.n_kv_heads), ml_ref.reshape(w.batch, w.n_kv_heads, k, 2), x["k"], ck_ref)
+        O.gather(mc_ref.reshape(w.batch, w.n_kv_heads), ml_ref.reshape(w.batch, w.n_kv_heads, k, 2), x["v"], cv_ref)
+        assert np.array_equal(H.host(ck), ck_ref) and np.array_equal(H.host(cv), cv_ref)
+        ref = O.attention(qf, x["k"], x["v"], sel_h.reshape(w.batch, w.n_kv_heads, k))
+        H.check_attention(H.host(out), ref, "bf16", "offload step %d" % t)
+        qf = f32_to_bf16_bits((H.as_f64(qf) + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32))
+
+
+def test_c1_tiny_end_to_end():
+    from nosa_inputs import WORKLOADS
+    w = WORKLOADS["C1"]
+    x = generate(w)
+    shape = H.shape_of(w)
+    q_dev = H.dev(x["q"])
+    kp = H.gpu_pool(shape, H.dev(x["k"]))
+    ws = N.workspace(shape)
+    sel, agn = H.gpu_select(shape, q_dev, kp, H.dev(x["evict"]), ws)
+    s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], 32), w.n_blocks, 2)
+    H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke)
+    out = H.gpu_decode(shape, q_dev, H.dev(x["k"]), H.dev(x["v"]), w.nbmax, sel, ws)
+    ref = O.attention(x["q"], x["k"], x["v"], H.host(sel).reshape(1, 1, -1))
+    H.check_attention(H.host(out), ref, "f32", "C1")
