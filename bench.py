@@ -1,0 +1,365 @@
+"""Benchmark of the NOSA decode-step hot path on one MI355X.
+
+A step is one decode step of one attention layer for every sequence of the batch, GPU-resident:
+nosa_select (pooled-key block scoring + query-agnostic / query-aware selection) followed by
+nosa_sparse_decode (split-K GQA attention over the selected blocks).  Pooled keys are state
+built once before timing (they change only when a block fills up).  tokens/s = batch / step time.
+
+  python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--config C2] [--also C3]
+                  [--no-cpu-baseline] [--offload]
+
+Prints one JSON line.  `value` is the headline workload (bs16 / 16K context by default); the
+same line carries the bs64 / 4K workload under "also", the decode kernel's roofline and the
+CPU oracle baseline.  --offload adds the 128-step offload loop (pinned host KV pool, 64-slot
+GPU cache) under "offload".
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_kernel_c2_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_decode_amd", "csrc", "decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+_INPUTS = {}
+
+
+def inputs(cfg):
+    """Generated host inputs of a workload, drawn once per process."""
+    from nosa_inputs import WORKLOADS, generate
+    if cfg not in _INPUTS:
+        t0 = time.time()
+        _INPUTS[cfg] = generate(WORKLOADS[cfg])
+        log("[bench] %s inputs generated in %.1fs" % (cfg, time.time() - t0))
+    return _INPUTS[cfg]
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per step (measurement section)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    R, k, d, B, Hq = w.rows, w.k, w.head_dim, w.batch, w.n_q_heads
+    kv_sel = R * k * 64 * d * eb * 2                      # selected K and V blocks
+    kp = R * w.n_blocks * 2 * d * 4                       # pooled keys, fp32, 2 sub-blocks per block
+    ev = R * w.n_blocks * 4                               # eviction scores
+    q = B * Hq * d * eb
+    o = B * Hq * d * eb
+    ids = R * k * 4                                       # selected ids
+    decode = kv_sel + q + o + ids                         # decode kernel: K/V, q, out, table
+    select = kp + q + ev + ids + R * w.ke * 4             # select kernel: pooled keys, q, e, out ids + state
+    return {"step": kv_sel + kp + ev + q + o + ids, "decode": decode, "select": select}
+
+
+def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_parts=0):
+    import numpy as np
+    import torch
+
+    import block_sparse_kv_decode_amd as N
+    from nosa_inputs import WORKLOADS
+
+    w = WORKLOADS[cfg]
+    x = inputs(cfg)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    shape = N.make_shape(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                         n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, sub_block_size=32,
+                         dtype=N.NOSA_BF16 if w.dtype == "bf16" else N.NOSA_F32, decode_splits=decode_splits,
+                         select_parts=select_parts)
+    q, k, v, ev = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["evict"])
+    R = w.rows
+    kp = torch.empty((R, w.nbmax * 2, w.head_dim), dtype=torch.float32, device="cuda")
+    ws = N.workspace(shape)
+    agn = torch.empty((R, max(w.ke, 1)), dtype=torch.int32, device="cuda")
+    sel = torch.empty((R, w.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+    N.nosa_pool_keys(shape, k, 0, w.nbmax, kp, sh)           # state, off the step timer
+    torch.cuda.synchronize()
+    scale = 1.0 / (w.head_dim ** 0.5)
+    # raw pointers, resolved once: the timed loop only enqueues
+    P = dict(q=q.data_ptr(), kp=kp.data_ptr(), ev=ev.data_ptr(), agn=agn.data_ptr(), sel=sel.data_ptr(),
+             ws=ws.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), out=out.data_ptr())
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        N.nosa_select(shape, P["q"], P["kp"], P["ev"], 0, P["agn"], P["sel"], P["ws"], sh)
+        if evs is not None:
+            evs[1].record(stream)
+        N.nosa_sparse_decode(shape, P["q"], P["k"], P["v"], w.nbmax, P["sel"], scale, P["out"], P["ws"], sh)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region 1: the plain step loop (headline value)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "tokens_per_s": w.batch * steps / wall}
+    if want_events:
+        # timed region 2: the same steps with HIP events around each kernel launch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        stp_ms = [e[0].elapsed_time(e[2]) for e in evs]
+        res.update({
+            "select_ms_mean": statistics.mean(sel_ms), "decode_ms_mean": statistics.mean(dec_ms),
+            "step_ms_median": statistics.median(stp_ms),
+            "step_ms_p10": float(np.percentile(stp_ms, 10)), "step_ms_p90": float(np.percentile(stp_ms, 90)),
+        })
+    res["bytes"] = algorithmic_bytes(w)
+    res["workload"] = w
+    return res
+
+
+def run_offload(steps_cap=None):
+    """C4: 128-step offload loop (pinned host KV pool, 64-slot cache per KV head)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_kv_decode_amd as N
+    from nosa_inputs import WORKLOADS, generate, visible_blocks
+
+    w = WORKLOADS["C4"]
+    x = generate(w)
+
+    def pin(a):
+        src = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        t = torch.empty(src.shape, dtype=torch.bfloat16, pin_memory=True)
+        t.copy_(src)
+        return t
+
+    hk, hv = pin(x["k"]), pin(x["v"])
+    kdev = torch.from_numpy(x["k"].view(np.int16)).view(torch.bfloat16).cuda()
+    shape0 = N.make_shape(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                          n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, cache_slots=w.cache_slots)
+    R, k, C = w.rows, w.k, w.cache_slots
+    kp = torch.empty((R, w.nbmax * 2, w.head_dim), dtype=torch.float32, device="cuda")
+    N.nosa_pool_keys(shape0, kdev, 0, w.nbmax, kp)
+    torch.cuda.synchronize()
+    del kdev
+    qs = torch.from_numpy(x["q_steps"].view(np.int16)).view(torch.bfloat16).cuda()
+    ev = torch.from_numpy(x["evict"]).cuda()
+    del x
+    ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    cv = torch.zeros_like(ck)
+    sob = torch.full((R, w.nbmax), -1, dtype=torch.int32, device="cuda")
+    bos = torch.full((R, C), -1, dtype=torch.int32, device="cuda")
+    table = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    mcnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    mlist = torch.empty((R, k, 2), dtype=torch.int32, device="cuda")
+    agn = torch.empty((R, w.ke), dtype=torch.int32, device="cuda")
+    sel = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = N.workspace(shape0)
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
+    scale = 1.0 / (w.head_dim ** 0.5)
+    steps = w.steps if steps_cap is None else min(w.steps, steps_cap)
+    step_ms, gather_ms, misses, prev = [], [], [], None
+    gam = []
+    n_prev = 0
+    for t in range(steps):
+        n = visible_blocks(w, t)
+        shape = shape0.copy(n_blocks=n)
+        e0, e1, e2, e3 = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e0.record(stream)
+        N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
+        N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, compute=stream,
+                            copy=copy_stream)
+        e1.record(stream)
+        N.nosa_sparse_decode(shape, qs[t], ck, cv, C, table, scale, out, ws, stream)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        step_ms.append(e0.elapsed_time(e2))
+        gather_ms.append(e0.elapsed_time(e1))
+        mc = mcnt.cpu().numpy()
+        misses.append(int(mc.sum()))
+        s_h = sel.cpu().numpy()
+        if prev is not None:
+            inter = [len(set(a.tolist()) & set(b.tolist())) / k for a, b in zip(prev, s_h)]
+            gam.extend(inter)
+        prev = s_h
+        n_prev = n
+    warm = slice(1, steps)
+    blk_bytes = 64 * w.head_dim * 2 * 2
+    fetched = [m * blk_bytes for m in misses]
+    mean_ms = statistics.mean(step_ms[warm])
+    return {
+        "workload": "C4: B16, GQA 32/8, d128, 16K ctx (+1 token/step), 32+32 blocks, 64-slot GPU cache per KV "
+                    "head, pinned host KV pool, %d steps" % steps,
+        "hit_rate_warm": 1.0 - statistics.mean(misses[warm]) / (R * k),
+        "fetched_bytes_per_step_warm": statistics.mean(fetched[warm]),
+        "cold_step_fetched_bytes": fetched[0],
+        "gamma_min": min(gam) if gam else None, "gamma_mean": statistics.mean(gam) if gam else None,
+        "step_ms_mean_warm": mean_ms,
+        "select_cache_gather_ms_mean_warm": statistics.mean(gather_ms[warm]),
+        "h2d_gbps_warm": statistics.mean(fetched[warm]) / (statistics.mean(gather_ms[warm]) * 1e-3) / 1e9,
+        "tokens_per_s": w.batch / (mean_ms * 1e-3),
+    }
+
+
+def measure_link_peak():
+    """Pinned host -> device copy bandwidth of a large hipMemcpyAsync (SDMA), GB/s."""
+    import torch
+    n = 512 << 20
+    h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    return 5 * n / (time.perf_counter() - t0) / 1e9
+
+
+def cpu_baseline(cfg, budget_s=10.0, max_s=30.0):
+    """The CPU oracle (fp64, OpenMP over rows) on the same workload: scores + selection + attention
+    per step, repeated until about budget_s of wall time."""
+    from nosa_inputs import WORKLOADS
+    from oracle import oracle as O
+
+    w = WORKLOADS[cfg]
+    x = inputs(cfg)
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        threads = min(threads, int(omp))
+    O.set_threads(threads)
+    kp = O.pool_keys(x["k"], 32)      # state, excluded like on the GPU
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.decode_step(x["q"], kp, x["evict"], x["k"], x["v"], w.n_blocks, w.kq, w.ke, 2)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el + el / reps > max_s:
+            break
+    return {"value": w.batch * reps / el, "unit": "tokens/s", "cores": O.get_threads(), "kind": "oracle",
+            "sample": "%d full %s decode steps (block scores + selection + attention, all %d rows), "
+                      "%.1f s wall, fp64" % (reps, cfg, w.rows, el)}
+
+
+def traffic_record():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs, if they were taken on
+    the current decode kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    rec = json.load(open(PROFILE_TRAFFIC))
+    src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if rec.get("decode_src_sha256") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def describe(w):
+    return "%s: B%d, GQA %d/%d, d%d, ctx %d, budget %d+%d blocks of 64 tokens, %s" % (
+        w.name, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.kq, w.ke, w.dtype)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--also", default="C3", help="comma list of extra resident workloads ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--offload", action="store_true", help="also run the 128-step offload loop")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard across GPUs "
+              "with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    main_res = run_resident(args.config, args.steps, args.warmup)
+    w = main_res["workload"]
+    by = main_res["bytes"]
+    dec_s = main_res["decode_ms_mean"] * 1e-3
+    achieved = by["decode"] / dec_s / 1e9
+    step_gbps = by["step"] / (main_res["ms_per_step"] * 1e-3) / 1e9
+    line = {
+        "metric": "sparse-decode tokens/s and achieved HBM GB/s (bs64 ctx4K, bs16 ctx16K)",
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded PCG64; K with per-block mean offsets, V ~N(0,1), eviction scores ~U(0,1))",
+        "config": {"workload": describe(w), "batch": w.batch, "context": w.n_tokens, "block": 64,
+                   "budget_blocks": w.k, "kq": w.kq, "ke": w.ke, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "layers": 1, "step": "nosa_select + nosa_sparse_decode"},
+        "step_hbm_gbps": step_gbps,
+        "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "step_algorithmic_bytes": by["step"],
+        "step_ms_median_events": main_res["step_ms_median"],
+        "step_ms_p10_p90_events": [main_res["step_ms_p10"], main_res["step_ms_p90"]],
+        "roofline": {
+            "kernel": "decode_kernel (nosa_sparse_decode)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(),
+            "algorithmic_bytes_per_launch": by["decode"], "avg_launch_ms": main_res["decode_ms_mean"],
+        },
+        "select_kernel": {"avg_launch_ms": main_res["select_ms_mean"], "algorithmic_bytes": by["select"],
+                          "achieved_gbps": by["select"] / (main_res["select_ms_mean"] * 1e-3) / 1e9},
+    }
+    also = {}
+    for cfg in [c for c in args.also.split(",") if c]:
+        r = run_resident(cfg, args.steps, args.warmup)
+        b2 = r["bytes"]
+        also[cfg] = {
+            "workload": describe(r["workload"]), "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+            "step_hbm_gbps": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
+            "step_hbm_frac": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "decode_gbps": b2["decode"] / (r["decode_ms_mean"] * 1e-3) / 1e9,
+            "decode_avg_launch_ms": r["decode_ms_mean"], "select_avg_launch_ms": r["select_ms_mean"],
+        }
+    if also:
+        line["also"] = also
+    if args.offload:
+        line["offload"] = run_offload()
+        line["offload"]["link_peak_gbps_sdma"] = measure_link_peak()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

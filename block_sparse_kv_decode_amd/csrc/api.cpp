@@ -44,6 +44,9 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Work distribution targets: enough workgroups to give every one of the 256 CUs two of them.
 constexpr int kTargetWorkgroups = 512;
 constexpr int kMinBlocksPerPart = 8;
+// A split shorter than this many blocks spends more time filling its load pipeline and merging
+// than it saves (measured on MI355X: 4-block splits lose to 8-block splits at 128K context).
+constexpr int kMinBlocksPerSplit = 8;
 
 int check_shape(const nosa_shape *s) {
     if (!s) return fail(NOSA_EINVAL, "shape is NULL");
@@ -89,6 +92,7 @@ struct SplitPlan {
 SplitPlan decode_plan(const nosa_shape *s) {
     const int R = rows_of(s), k = s->kq + s->ke;
     int S = s->decode_splits > 0 ? s->decode_splits : (kTargetWorkgroups + R - 1) / R;
+    if (s->decode_splits <= 0 && S > k / kMinBlocksPerSplit) S = k / kMinBlocksPerSplit;
     if (S < 1) S = 1;
     if (S > k) S = k;
     const int nbs = (k + S - 1) / S;
@@ -116,7 +120,7 @@ PartPlan select_plan(const nosa_shape *s) {
 }
 
 struct WsLayout {
-    size_t scores, scnt, part, dcnt, total;
+    size_t scores, part, total;
 };
 
 WsLayout ws_layout(const nosa_shape *s) {
@@ -126,12 +130,8 @@ WsLayout ws_layout(const nosa_shape *s) {
     size_t off = 0;
     L.scores = off;
     off = round_up(off + R * (size_t)s->n_blocks_max * sizeof(float), kAlign);
-    L.scnt = off;
-    off = round_up(off + R * sizeof(uint32_t), kAlign);
     L.part = off;
     off = round_up(off + R * (size_t)dp.S * group_of(s) * (size_t)(s->head_dim + 2) * sizeof(float), kAlign);
-    L.dcnt = off;
-    off = round_up(off + R * sizeof(uint32_t), kAlign);
     L.total = off;
     return L;
 }
@@ -227,7 +227,6 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
     a.agn = agn_state;
     a.sel = selected;
     a.scores = scores_only ? scores_out : (float *)((char *)ws + L.scores);
-    a.cnt = (uint32_t *)((char *)ws + L.scnt);
     a.Hq = shape->n_q_heads;
     a.Hkv = shape->n_kv_heads;
     a.G = group_of(shape);
@@ -356,7 +355,6 @@ int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_sto
     a.table = block_table;
     a.out = out;
     a.part = (float *)((char *)ws + L.part);
-    a.cnt = (uint32_t *)((char *)ws + L.dcnt);
     a.Hq = shape->n_q_heads;
     a.Hkv = shape->n_kv_heads;
     a.k_sel = shape->kq + shape->ke;

@@ -19,8 +19,8 @@
 //               The probabilities travel from the QK layout through 16 x G floats of LDS.
 //   Prefetch  : K and V of block j+1 are loaded into registers while block j is computed.
 // End of split: lane reduction, a 4-wave merge through LDS, then either the final output
-// (S = 1) or a (max, sum, acc) partial; the split that arrives last (agent-scope counter)
-// merges the S partials of its row and writes the output.
+// (S = 1) or a (max, sum, acc) partial in the workspace, merged by combine_kernel (one
+// workgroup per row) with the same online-softmax rule.  No workgroup waits on another.
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
@@ -139,7 +139,6 @@ __global__ __launch_bounds__(256, (G >= 8 || sizeof(T) * D > 256) ? 1 : 2) void 
     __shared__ __align__(16) float p_lds[kWaves][kTokPerWave][G];
     __shared__ float w_m[kWaves][G], w_l[kWaves][G];
     __shared__ __align__(16) float w_acc[kWaves][G][D];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
@@ -240,7 +239,6 @@ __global__ __launch_bounds__(256, (G >= 8 || sizeof(T) * D > 256) ? 1 : 2) void 
 
     // ---- merge the 4 waves -----------------------------------------------------------------
     const size_t out_base = (size_t)(b * a.Hq + g * G) * D;
-    float *part = a.part + (size_t)(row * a.S + sp) * G * (D + 2);
     for (int idx = tid; idx < G * D; idx += 256) {
         const int h = idx / D, dd = idx - h * D;
         float M = w_m[0][h];
@@ -256,45 +254,44 @@ __global__ __launch_bounds__(256, (G >= 8 || sizeof(T) * D > 256) ? 1 : 2) void 
         if (a.S == 1) {
             store_elem<T>(a.out, out_base + idx, A / L);
         } else {
-            part[h * (D + 2) + 2 + dd] = A;
+            float *part = a.part + ((size_t)(row * a.S + sp) * G + h) * (D + 2);
+            part[2 + dd] = A;
             if (dd == 0) {
-                part[h * (D + 2) + 0] = M;
-                part[h * (D + 2) + 1] = L;
+                part[0] = M;
+                part[1] = L;
             }
         }
     }
-    if (a.S == 1) return;
+}
 
-    // ---- the last split of the row merges the S partials -------------------------------------
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&a.cnt[row], 1u);
-        s_last = (prev == (uint32_t)(a.S - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+// Merges the S split partials (max, sum, acc) of every row into the output.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+    const int row = blockIdx.x;
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
+    const size_t out_base = (size_t)(b * a.Hq + g * G) * D;
     const float *rp = a.part + (size_t)row * a.S * G * (D + 2);
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
         const int h = idx / D, dd = idx - h * D;
         float M = -INFINITY;
-        for (int s = 0; s < a.S; ++s) M = fmaxf(M, load_agent(rp + (size_t)(s * G + h) * (D + 2)));
+        for (int s = 0; s < a.S; ++s) M = fmaxf(M, rp[(size_t)(s * G + h) * (D + 2)]);
         float L = 0.0f, A = 0.0f;
         for (int s = 0; s < a.S; ++s) {
             const float *ps = rp + (size_t)(s * G + h) * (D + 2);
-            const float f = fast_exp2(load_agent(ps) - M);
-            L = fmaf(load_agent(ps + 1), f, L);
-            A = fmaf(load_agent(ps + 2 + dd), f, A);
+            const float f = fast_exp2(ps[0] - M);
+            L = fmaf(ps[1], f, L);
+            A = fmaf(ps[2 + dd], f, A);
         }
         store_elem<T>(a.out, out_base + idx, A / L);
     }
-    if (tid == 0) __hip_atomic_store(&a.cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st) {
     decode_kernel<T, D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.S == 1) return e;
+    combine_kernel<T, D, G><<<dim3((unsigned)rows), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 

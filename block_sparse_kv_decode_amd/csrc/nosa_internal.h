@@ -28,7 +28,6 @@ struct SelectArgs {
     int32_t *agn;         // [R, ke]
     int32_t *sel;         // [R, kq + ke]
     float *scores;        // [R, scores_stride] global block scores (parts > 1, or scores-only mode)
-    uint32_t *cnt;        // [R] arrival counters (parts > 1)
     int Hq, Hkv, G;
     int n_blocks, n_blocks_max, kq, ke, n_prev;
     int parts;            // workgroups per row
@@ -62,7 +61,6 @@ struct DecodeArgs {
     const int32_t *table; // [R, k_sel]
     void *out;            // [B, Hq, d]
     float *part;          // [R, S, G, d + 2] split partials (S > 1)
-    uint32_t *cnt;        // [R] arrival counters (S > 1)
     int Hq, Hkv, k_sel, store_blocks;
     int S;                // splits per row
     int nbs;              // blocks per split

@@ -31,10 +31,10 @@
  *     n_q_heads / n_kv_heads in {1, 2, 4, 8}; 1 <= kq + ke <= n_blocks <= n_blocks_max <= 16384;
  *     cache_slots >= kq + ke (for nosa_cache_update).  Anything else returns NOSA_EUNSUPPORTED
  *     or NOSA_EINVAL.
- *   - Workspace: nosa_workspace_bytes() bytes of device memory, 256-byte aligned, zero-filled once
- *     by the caller before its first use.  Each call leaves the workspace's internal counters at
- *     zero again, so it can be reused without clearing.  Calls that share a workspace must be
- *     ordered (same stream, or synchronised); concurrent calls on one workspace race.
+ *   - Workspace: nosa_workspace_bytes() bytes of device memory, 256-byte aligned, no initial
+ *     contents required (it holds block scores and split-K partials between the kernels of one
+ *     call).  Calls that share a workspace must be ordered (same stream, or synchronised);
+ *     concurrent calls on one workspace race.
  */
 #ifndef NOSA_H
 #define NOSA_H

@@ -37,11 +37,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     flat_o = out.reshape(-1)
     step = 1 << 24
     for s in range(0, flat_u.size, step):
-        v = flat_u[s:s + step].astype(np.uint64)
-        nan = (v & 0x7FFFFFFF) > 0x7F800000
-        r = (v + 0x7FFF + ((v >> 16) & 1)) >> 16
-        r = np.where(nan, (v >> 16) | 0x40, r)
-        flat_o[s:s + step] = r.astype(np.uint16)
+        v = flat_u[s:s + step]
+        # finite values cannot overflow uint32 here; NaNs are patched afterwards
+        r = ((v + np.uint32(0x7FFF) + ((v >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+        nan = (v & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        if nan.any():
+            r[nan] = ((v[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+        flat_o[s:s + step] = r
     return out
 
 

@@ -110,6 +110,8 @@ def test_c4_offload_loop():
                         assert np.array_equal(cvh[b, g, s_], x["v"][b, g, blk])
         prev_sel = sel_h
         n_prev = n
+        if t % 32 == 0:
+            print("C4 step %d ok" % t, flush=True)
     g = np.concatenate(gammas)
     print("C4 gamma min %.3f mean %.3f; hit rate (warm) %.3f" % (g.min(), g.mean(), np.mean(hits[1:]) / k))
     assert g.min() >= w.ke / k - 1e-12
