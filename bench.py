@@ -295,6 +295,8 @@ def main():
     ap.add_argument("--also", default="C3", help="comma list of extra resident workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--offload", action="store_true", help="also run the 128-step offload loop")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise copy of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard across GPUs "
@@ -303,6 +305,17 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 64 << 20                      # float32 elements: 256 MiB read + 256 MiB written per launch
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_kernel": "elementwise mul by 1 (float32)", "bytes_read_per_launch": 4 * n,
+                          "bytes_written_per_launch": 4 * n, "launches": 5}), flush=True)
+        return
 
     main_res = run_resident(args.config, args.steps, args.warmup)
     w = main_res["workload"]
@@ -332,7 +345,7 @@ def main():
         "step_ms_median_events": main_res["step_ms_median"],
         "step_ms_p10_p90_events": [main_res["step_ms_p10"], main_res["step_ms_p90"]],
         "roofline": {
-            "kernel": "decode_kernel (nosa_sparse_decode)",
+            "kernel": "nosa_sparse_decode call: decode_mfma_kernel + combine_kernel (split-K merge)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(),
             "algorithmic_bytes_per_launch": by["decode"], "avg_launch_ms": main_res["decode_ms_mean"],

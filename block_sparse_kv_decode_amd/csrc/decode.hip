@@ -9,24 +9,33 @@
 // row's block table.  Wave w owns tokens [16w, 16w + 16) of every block, so the four waves run
 // with no barrier until the end of the split, each with its own online-softmax state for the G
 // query heads of the row (the G heads reuse every K/V byte: the GQA saving).
-//   QK layout : 4 lanes per token, each holding CPL 16-byte chunks (64 contiguous bytes per
-//               token and load); q . K with packed bf16 dot products (fp32 FMAs for fp32 data),
-//               reduced over the 4 lanes with two DPP adds.
-//   softmax   : scores in the log2 domain (scale * log2 e folded in), block max over the wave's
-//               16 tokens (DPP + lane swaps), running max / sum per head, exp2.
-//   PV layout : the wave's 16 V rows are loaded as fully contiguous 1 KiB lines; a lane owns one
-//               16-byte column chunk of several tokens and accumulates G x (chunk) fp32 outputs.
-//               The probabilities travel from the QK layout through 16 x G floats of LDS.
-//   Prefetch  : K and V of block j+1 are loaded into registers while block j is computed.
+//   QK, bf16 : one 16x16x32 bf16 MFMA per 32 dims: A = the wave's 16 key rows (each lane loads a
+//              16-byte chunk; four lanes cover 64 contiguous bytes of a row), B = the G query
+//              heads (columns G..15 zero), fp32 accumulate.  The G x 16 products of a block are a
+//              small dense contraction; on the matrix cores it frees the VALU for the softmax and
+//              P.V, and keeps q in 16 registers instead of 64.
+//   QK, fp32 : VALU dot products, 4 lanes per key row, reduced with two DPP adds.
+//   softmax  : scores in the log2 domain (scale * log2 e folded in).  The running max only moves
+//              when some lane's score exceeds it (a wave-wide vote), so most blocks skip the
+//              cross-lane max and the accumulator rescale.
+//   P.V      : the wave's 16 V rows are loaded as contiguous 1 KiB lines; a lane owns one 16-byte
+//              column chunk of several rows and accumulates G x chunk fp32 outputs (VALU FMAs:
+//              V would need a transpose to feed the matrix cores).  Probabilities travel through
+//              16 x G floats of LDS.
+//   Prefetch : K and V of the next blocks are loaded into registers while a block is computed
+//              (two blocks ahead for bf16, one for fp32).
 // End of split: lane reduction, a 4-wave merge through LDS, then either the final output
-// (S = 1) or a (max, sum, acc) partial in the workspace, merged by combine_kernel (one
-// workgroup per row) with the same online-softmax rule.  No workgroup waits on another.
+// (S = 1) or a (max, sum, acc) partial in the workspace, merged by combine_kernel with the same
+// online-softmax rule.  No workgroup waits on another.
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
 namespace nosa {
 
 namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kTokPerWave = kBlockTokens / kWaves;   // 16
@@ -42,14 +51,7 @@ struct Geom {
     static_assert(NC == 8 || NC == 16 || NC == 32, "unsupported row size");
 };
 
-__device__ __forceinline__ float dot16(const uint4 &a, const uint4 &b, float acc, uint16_t) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
-    return acc;
-}
-__device__ __forceinline__ float dot16(const uint4 &a, const uint4 &b, float acc, float) {
+__device__ __forceinline__ float dot16_f32(const uint4 &a, const uint4 &b, float acc) {
     acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
     acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
     acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
@@ -68,52 +70,15 @@ __device__ __forceinline__ void unpack16(const uint4 &x, float *v, float) {
     v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
 }
 
-template <typename T, int D, int G>
-struct WaveState {
-    float m[G];                          // running max (log2 domain), wave-uniform
-    float lq[G];                         // running sum of p for this lane's QK token
-    float acc[G][Geom<T, D>::EPC];       // running sum of p * V for this lane's PV column chunk
-};
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
 
-// One 64-token block: this wave's 16-token slice.
+// acc[h][e] += p[tok][h] * V[tok][chunk e] over this lane's PV tokens of the block.
 template <typename T, int D, int G>
-__device__ __forceinline__ void process_block(WaveState<T, D, G> &st, const uint4 (&qf)[G][Geom<T, D>::CPL],
-                                              const uint4 (&kk)[Geom<T, D>::CPL], const uint4 (&vv)[Geom<T, D>::CPL],
-                                              float (*pl)[G], float sl2, int sub, int tq, int tpv) {
+__device__ __forceinline__ void pv_accumulate(const float (*pl)[G], int tpv, const uint4 (&vv)[Geom<T, D>::CPL],
+                                              float (&acc)[G][Geom<T, D>::EPC]) {
     using Gm = Geom<T, D>;
-    float z[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < Gm::CPL; ++i) s = dot16(qf[h][i], kk[i], s, T());
-        s += dpp<kDppQuadXor1>(s);
-        s += dpp<kDppQuadXor2>(s);
-        z[h] = s * sl2;
-    }
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float bm = fmaxf(z[h], dpp<kDppRowRor4>(z[h]));
-        bm = fmaxf(bm, dpp<kDppRowRor8>(bm));
-        bm = fmaxf(bm, xor_lane(bm, 16));
-        bm = fmaxf(bm, xor_lane(bm, 32));
-        const float mn = fmaxf(st.m[h], bm);
-        alpha[h] = fast_exp2(st.m[h] - mn);
-        st.m[h] = mn;
-        const float p = fast_exp2(z[h] - mn);
-        st.lq[h] = fmaf(st.lq[h], alpha[h], p);
-        z[h] = p;
-    }
-    if (sub == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) pl[tq][h] = z[h];
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < Gm::EPC; ++e) st.acc[h][e] *= alpha[h];
 #pragma unroll
     for (int i = 0; i < Gm::CPL; ++i) {
         const int tok = i * Gm::TPI + tpv;
@@ -125,131 +90,64 @@ __device__ __forceinline__ void process_block(WaveState<T, D, G> &st, const uint
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < Gm::EPC; ++e) st.acc[h][e] = fmaf(p[h], v[e], st.acc[h][e]);
+            for (int e = 0; e < Gm::EPC; ++e) acc[h][e] = fmaf(p[h], v[e], acc[h][e]);
     }
-    wave_lds_sync();
 }
 
-}  // namespace
+template <int D, int G>
+struct SplitShared {
+    __align__(16) float p[kWaves][kTokPerWave][G];
+    float m[kWaves][G], l[kWaves][G];
+    __align__(16) float acc[kWaves][G][D];
+};
 
+// End of a split: reduce the lane accumulators, merge the 4 waves, write the output (S == 1) or
+// the split's (max, sum, acc) partial.  m_h / l_h: this wave's per-head running max / sum.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256, (G >= 8 || sizeof(T) * D > 256) ? 1 : 2) void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void finish_split(const DecodeArgs &a, int row, int sp, const float (&m_h)[G],
+                                             const float (&l_h)[G], float (&acc)[G][Geom<T, D>::EPC],
+                                             SplitShared<D, G> &sh) {
     using Gm = Geom<T, D>;
-    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB, TPI = Gm::TPI;
-    __shared__ __align__(16) float p_lds[kWaves][kTokPerWave][G];
-    __shared__ float w_m[kWaves][G], w_l[kWaves][G];
-    __shared__ __align__(16) float w_acc[kWaves][G][D];
-
+    constexpr int NC = Gm::NC, EPC = Gm::EPC;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
-    const int b = row / a.Hkv, g = row - b * a.Hkv;
-    const int sub = lane & 3, tq = lane >> 2;          // QK layout
-    const int cpv = lane % NC, tpv = lane / NC;        // PV layout
-    const int j0 = sp * a.nbs, j1 = min(a.k_sel, j0 + a.nbs);
-
-    uint4 qf[G][CPL];
-    {
-        const char *qrow = (const char *)a.q + (size_t)(b * a.Hq + g * G) * RB;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) qf[h][i] = *(const uint4 *)(qrow + h * RB + (sub + 4 * i) * 16);
-    }
-
-    const size_t blk_bytes = (size_t)kBlockTokens * RB;
-    const char *kbase = (const char *)a.k + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
-    const char *vbase = (const char *)a.v + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
-    int kofs[CPL], vofs[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        kofs[i] = tq * RB + (sub + 4 * i) * 16;
-        vofs[i] = (i * TPI + tpv) * RB + cpv * 16;
-    }
-
-    WaveState<T, D, G> st;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        st.m[h] = -INFINITY;
-        st.lq[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) st.acc[h][e] = 0.0f;
-    }
-
-    const int32_t *tab = a.table + (size_t)row * a.k_sel;
-    uint4 kc[CPL], vc[CPL], kn[CPL], vn[CPL];
-    auto load = [&](int j, uint4(&kk)[CPL], uint4(&vv)[CPL]) -> bool {
-        const int blk = tab[j];
-        if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
-        const char *kp = kbase + (size_t)blk * blk_bytes;
-        const char *vp = vbase + (size_t)blk * blk_bytes;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) kk[i] = *(const uint4 *)(kp + kofs[i]);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) vv[i] = *(const uint4 *)(vp + vofs[i]);
-        return true;
-    };
-
-    float(*pl)[G] = p_lds[w];
-    int j = j0;
-    bool okc = (j < j1) ? load(j, kc, vc) : false, okn = false;
-    while (j < j1) {
-        if (j + 1 < j1) okn = load(j + 1, kn, vn);
-        if (okc) process_block<T, D, G>(st, qf, kc, vc, pl, a.sl2, sub, tq, tpv);
-        if (++j >= j1) break;
-        if (j + 1 < j1) okc = load(j + 1, kc, vc);
-        if (okn) process_block<T, D, G>(st, qf, kn, vn, pl, a.sl2, sub, tq, tpv);
-        ++j;
-    }
-
-    // ---- reduce within the wave ----------------------------------------------------------
-    float l[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float x = st.lq[h];                  // identical in the 4 lanes of a token
-        x += dpp<kDppRowRor4>(x);
-        x += dpp<kDppRowRor8>(x);
-        x += xor_lane(x, 16);
-        x += xor_lane(x, 32);
-        l[h] = x;
-    }
+    const int cpv = lane % NC, tpv = lane / NC;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-            float x = st.acc[h][e];
+            float x = acc[h][e];
             if (NC <= 8) x += dpp<kDppRowRor8>(x);
             if (NC <= 16) x += xor_lane(x, 16);
             x += xor_lane(x, 32);
-            st.acc[h][e] = x;
+            acc[h][e] = x;
         }
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            w_m[w][h] = st.m[h];
-            w_l[w][h] = l[h];
+            sh.m[w][h] = m_h[h];
+            sh.l[w][h] = l_h[h];
         }
     }
     if (tpv == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) w_acc[w][h][cpv * EPC + e] = st.acc[h][e];
+            for (int e = 0; e < EPC; ++e) sh.acc[w][h][cpv * EPC + e] = acc[h][e];
     }
     __syncthreads();
-
-    // ---- merge the 4 waves -----------------------------------------------------------------
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
     const size_t out_base = (size_t)(b * a.Hq + g * G) * D;
     for (int idx = tid; idx < G * D; idx += 256) {
         const int h = idx / D, dd = idx - h * D;
-        float M = w_m[0][h];
+        float M = sh.m[0][h];
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, w_m[ww][h]);
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sh.m[ww][h]);
         float L = 0.0f, A = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = fast_exp2(w_m[ww][h] - M);
-            L = fmaf(w_l[ww][h], f, L);
-            A = fmaf(w_acc[ww][h][dd], f, A);
+            const float f = fast_exp2(sh.m[ww][h] - M);
+            L = fmaf(sh.l[ww][h], f, L);
+            A = fmaf(sh.acc[ww][h][dd], f, A);
         }
         if (a.S == 1) {
             store_elem<T>(a.out, out_base + idx, A / L);
@@ -264,34 +162,307 @@ __global__ __launch_bounds__(256, (G >= 8 || sizeof(T) * D > 256) ? 1 : 2) void 
     }
 }
 
-// Merges the S split partials (max, sum, acc) of every row into the output.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-    const int row = blockIdx.x;
+}  // namespace
+
+// ---- bf16: QK on the matrix cores -----------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+    using Gm = Geom<uint16_t, D>;
+    constexpr int KS = D / 32;                        // 32-dim MFMA steps
+    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB, TPI = Gm::TPI;
+    static_assert(CPL == KS, "bf16 rows: one V chunk per MFMA step");
+    __shared__ SplitShared<D, G> sh;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
     const int b = row / a.Hkv, g = row - b * a.Hkv;
-    const size_t out_base = (size_t)(b * a.Hq + g * G) * D;
-    const float *rp = a.part + (size_t)row * a.S * G * (D + 2);
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int h = idx / D, dd = idx - h * D;
-        float M = -INFINITY;
-        for (int s = 0; s < a.S; ++s) M = fmaxf(M, rp[(size_t)(s * G + h) * (D + 2)]);
-        float L = 0.0f, A = 0.0f;
-        for (int s = 0; s < a.S; ++s) {
-            const float *ps = rp + (size_t)(s * G + h) * (D + 2);
-            const float f = fast_exp2(ps[0] - M);
-            L = fmaf(ps[1], f, L);
-            A = fmaf(ps[2 + dd], f, A);
+    const int j16 = lane & 15, grp = lane >> 4;       // MFMA layout: column (head) / k-group
+    const int cpv = lane % NC, tpv = lane / NC;       // PV layout
+    const int j0 = sp * a.nbs, j1 = min(a.k_sel, j0 + a.nbs);
+
+    // B operand: q of head j16 (zero columns beyond G), dims 32 ks + 8 grp .. + 8
+    bf16x8_t qb[KS];
+    {
+        const char *qrow = (const char *)a.q + (size_t)(b * a.Hq + g * G + (j16 < G ? j16 : 0)) * RB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            if (j16 < G) x = *(const uint4 *)(qrow + (4 * ks + grp) * 16);
+            qb[ks] = __builtin_bit_cast(bf16x8_t, x);
         }
-        store_elem<T>(a.out, out_base + idx, A / L);
     }
+
+    const size_t blk_bytes = (size_t)kBlockTokens * RB;
+    const char *kbase = (const char *)a.k + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
+    const char *vbase = (const char *)a.v + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
+    int kofs[KS], vofs[CPL];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] = j16 * RB + (4 * ks + grp) * 16;   // A operand: key row j16
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) vofs[i] = (i * TPI + tpv) * RB + cpv * 16;
+
+    float m = -INFINITY;          // running max of head j16 (lanes j16 < G)
+    float lq = 0.0f;              // running sum of p over this lane's 4 tokens of head j16
+    float acc[G][EPC];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
+    float(*pl)[G] = sh.p[w];
+    const float sl2 = a.sl2;
+
+    auto process = [&](const uint4(&kk)[KS], const uint4(&vv)[CPL]) {
+        floatx4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk[ks]), qb[ks], c, 0, 0, 0);
+        // lane holds S[token 4 grp + e][head j16]
+        float z[4];
+        bool up = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            z[e] = c[e] * sl2;
+            up |= (j16 < G) && (z[e] > m);
+        }
+        const bool rescale = __any(up);
+        float alpha = 1.0f;
+        if (rescale) {
+            float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+            bm = fmaxf(bm, xor_lane(bm, 16));
+            bm = fmaxf(bm, xor_lane(bm, 32));
+            const float mn = fmaxf(m, bm);
+            alpha = fast_exp2(m - mn);
+            m = mn;
+        }
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            z[e] = fast_exp2(z[e] - m);
+            ps += z[e];
+        }
+        lq = rescale ? fmaf(lq, alpha, ps) : lq + ps;
+        if (j16 < G) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pl[4 * grp + e][j16] = z[e];
+        }
+        wave_lds_sync();
+        if (rescale) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float ah = readlane_f(alpha, h);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[h][e] *= ah;
+            }
+        }
+        pv_accumulate<uint16_t, D, G>(pl, tpv, vv, acc);
+        wave_lds_sync();
+    };
+
+    const int32_t *tab = a.table + (size_t)row * a.k_sel;
+    auto load = [&](int j, uint4(&kk)[KS], uint4(&vv)[CPL]) -> bool {
+        const int blk = tab[j];
+        if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
+        const char *kp = kbase + (size_t)blk * blk_bytes;
+        const char *vp = vbase + (size_t)blk * blk_bytes;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kk[ks] = *(const uint4 *)(kp + kofs[ks]);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) vv[i] = *(const uint4 *)(vp + vofs[i]);
+        return true;
+    };
+
+    // three register buffers: blocks j+1 and j+2 are in flight while block j is computed
+    uint4 kb0[KS], vb0[CPL], kb1[KS], vb1[CPL], kb2[KS], vb2[CPL];
+    int j = j0;
+    bool o0 = (j < j1) ? load(j, kb0, vb0) : false;
+    bool o1 = (j + 1 < j1) ? load(j + 1, kb1, vb1) : false;
+    bool o2 = false;
+    while (j < j1) {
+        if (j + 2 < j1) o2 = load(j + 2, kb2, vb2);
+        if (o0) process(kb0, vb0);
+        if (++j >= j1) break;
+        if (j + 2 < j1) o0 = load(j + 2, kb0, vb0);
+        if (o1) process(kb1, vb1);
+        if (++j >= j1) break;
+        if (j + 2 < j1) o1 = load(j + 2, kb1, vb1);
+        if (o2) process(kb2, vb2);
+        ++j;
+    }
+
+    // per-head max and sum of this wave: lanes j16 = h of the four k-groups
+    float lt = lq;
+    lt += xor_lane(lt, 16);
+    lt += xor_lane(lt, 32);
+    float m_h[G], l_h[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_h[h] = readlane_f(m, h);
+        l_h[h] = readlane_f(lt, h);
+    }
+    finish_split<uint16_t, D, G>(a, row, sp, m_h, l_h, acc, sh);
+}
+
+// ---- fp32: QK on the VALU ------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_kernel(DecodeArgs a) {
+    using Gm = Geom<float, D>;
+    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB, TPI = Gm::TPI;
+    __shared__ SplitShared<D, G> sh;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
+    const int sub = lane & 3, tq = lane >> 2;          // QK layout: 4 lanes per key row
+    const int cpv = lane % NC, tpv = lane / NC;        // PV layout
+    const int j0 = sp * a.nbs, j1 = min(a.k_sel, j0 + a.nbs);
+
+    uint4 qf[G][CPL];
+    {
+        const char *qrow = (const char *)a.q + (size_t)(b * a.Hq + g * G) * RB;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) qf[h][i] = *(const uint4 *)(qrow + h * RB + (sub + 4 * i) * 16);
+    }
+    const size_t blk_bytes = (size_t)kBlockTokens * RB;
+    const char *kbase = (const char *)a.k + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
+    const char *vbase = (const char *)a.v + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
+    int kofs[CPL], vofs[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        kofs[i] = tq * RB + (sub + 4 * i) * 16;
+        vofs[i] = (i * TPI + tpv) * RB + cpv * 16;
+    }
+
+    float m[G], lq[G], acc[G][EPC];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        lq[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
+    }
+    float(*pl)[G] = sh.p[w];
+    const float sl2 = a.sl2;
+
+    auto process = [&](const uint4(&kk)[CPL], const uint4(&vv)[CPL]) {
+        float z[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) s = dot16_f32(qf[h][i], kk[i], s);
+            s += dpp<kDppQuadXor1>(s);
+            s += dpp<kDppQuadXor2>(s);
+            z[h] = s * sl2;
+        }
+        bool up = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) up |= z[h] > m[h];
+        float alpha[G];
+        const bool rescale = __any(up);
+        if (rescale) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float bm = fmaxf(z[h], dpp<kDppRowRor4>(z[h]));
+                bm = fmaxf(bm, dpp<kDppRowRor8>(bm));
+                bm = fmaxf(bm, xor_lane(bm, 16));
+                bm = fmaxf(bm, xor_lane(bm, 32));
+                const float mn = fmaxf(m[h], bm);
+                alpha[h] = fast_exp2(m[h] - mn);
+                m[h] = mn;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = fast_exp2(z[h] - m[h]);
+            lq[h] = rescale ? fmaf(lq[h], alpha[h], p) : lq[h] + p;
+            z[h] = p;
+        }
+        if (sub == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) pl[tq][h] = z[h];
+        }
+        wave_lds_sync();
+        if (rescale) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha[h];
+        }
+        pv_accumulate<float, D, G>(pl, tpv, vv, acc);
+        wave_lds_sync();
+    };
+
+    const int32_t *tab = a.table + (size_t)row * a.k_sel;
+    auto load = [&](int j, uint4(&kk)[CPL], uint4(&vv)[CPL]) -> bool {
+        const int blk = tab[j];
+        if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
+        const char *kp = kbase + (size_t)blk * blk_bytes;
+        const char *vp = vbase + (size_t)blk * blk_bytes;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) kk[i] = *(const uint4 *)(kp + kofs[i]);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) vv[i] = *(const uint4 *)(vp + vofs[i]);
+        return true;
+    };
+    uint4 kc[CPL], vc[CPL], kn[CPL], vn[CPL];
+    int j = j0;
+    bool okc = (j < j1) ? load(j, kc, vc) : false, okn = false;
+    while (j < j1) {
+        if (j + 1 < j1) okn = load(j + 1, kn, vn);
+        if (okc) process(kc, vc);
+        if (++j >= j1) break;
+        if (j + 1 < j1) okc = load(j + 1, kc, vc);
+        if (okn) process(kn, vn);
+        ++j;
+    }
+
+    float m_h[G], l_h[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float x = lq[h];                  // identical in the 4 lanes of a key row
+        x += dpp<kDppRowRor4>(x);
+        x += dpp<kDppRowRor8>(x);
+        x += xor_lane(x, 16);
+        x += xor_lane(x, 32);
+        l_h[h] = x;
+        m_h[h] = m[h];
+    }
+    finish_split<float, D, G>(a, row, sp, m_h, l_h, acc, sh);
+}
+
+// Merges the S split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
+    const int row = blockIdx.x / G, h = blockIdx.x - row * G;
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
+    const int dd = threadIdx.x;
+    const float *rp = a.part + ((size_t)row * a.S * G + h) * (D + 2);
+    const size_t stride = (size_t)G * (D + 2);
+    float M = -INFINITY, L = 0.0f, A = 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < a.S; ++s) {
+        const float *ps = rp + s * stride;
+        const float ms = ps[0], ls = ps[1], as = ps[2 + dd];
+        const float mn = fmaxf(M, ms);
+        const float fo = fast_exp2(M - mn), fn = fast_exp2(ms - mn);
+        L = L * fo + ls * fn;
+        A = A * fo + as * fn;
+        M = mn;
+    }
+    store_elem<T>(a.out, (size_t)(b * a.Hq + g * G + h) * D + dd, A / L);
 }
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st) {
-    decode_kernel<T, D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
+    if (sizeof(T) == 2)
+        decode_mfma_kernel<D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
+    else
+        decode_valu_kernel<D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.S == 1) return e;
-    combine_kernel<T, D, G><<<dim3((unsigned)rows), dim3(256), 0, st>>>(a);
+    combine_kernel<T, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
     return hipGetLastError();
 }
 

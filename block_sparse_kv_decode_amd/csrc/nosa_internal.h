@@ -69,7 +69,8 @@ struct DecodeArgs {
 
 // Each launcher returns hipSuccess or the error of the launch.
 hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_t st);
-hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, hipStream_t st);
+// fused_threads: workgroup size (256 or 1024) of the one-workgroup-per-row plan (parts == 1).
+hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads, hipStream_t st);
 size_t select_lds_bytes(int n_blocks);
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
 hipError_t launch_gather(const GatherArgs &a, int rows, hipStream_t st);

@@ -9,23 +9,24 @@
 //   [P4] gist.science technical summary, Method 1 (strict eviction: a unit left out at one step
 //        is never selected again by the query-agnostic part; locality >= ke / k).
 //
-// Scoring (256 threads, 4 waves).  The group query qs = sum of the row's G query heads (fp32) is
-//   dotted with every pooled sub-block key; eight lanes share one fp32 sub-block row (16-byte
-//   loads, 128 contiguous bytes per lane group and load), reduce with three DPP adds and
-//   max-pool the block's sub-blocks with DPP / lane swaps.  Each wave keeps four row groups of
-//   loads in flight.
+// Scoring.  Every lane builds its slice of the group query qs = sum of the row's G query heads
+//   (fp32) straight from global memory, so the pooled-key loads are issued without waiting on a
+//   barrier.  Eight lanes share one fp32 sub-block row (16-byte loads, 128 contiguous bytes per
+//   lane group and load), reduce with three DPP adds and max-pool the block's sub-blocks with DPP
+//   and lane swaps; each wave keeps four groups of eight rows in flight.
 // Selection (one workgroup per row, in LDS).
 //   Gamma_e: top-ke by eviction score among all visible blocks (first step) or among the
 //            previous Gamma_e plus the newly visible blocks (strict eviction);
 //   Gamma_q: top-kq by block score among the visible blocks outside Gamma_e.
 //   Exact top-k on unique 64-bit keys (order-preserving score bits, then the inverted block id,
 //   so equal scores go to the lower id): rows of up to 512 blocks rank every candidate against
-//   all others in one pass; longer rows use a radix select (four 8-bit digit passes over an LDS
-//   histogram) with the id tie rule applied by a scan.  Outputs are compacted in ascending id.
-// Launch plans.  A row that one workgroup scores (parts == 1) is scored and selected by that
-//   workgroup ("fused").  Longer rows are scored by `parts` workgroups into the workspace and
-//   selected by a second kernel with one workgroup per row; no cross-workgroup synchronisation
-//   happens inside a kernel.
+//   all others, several lanes sharing each count; longer rows first drop every key below a bound
+//   taken from 256 chunk maxima and rank the survivors (radix select as the fallback).  Outputs
+//   are compacted in ascending block id.
+// Launch plans (chosen on the host).  "fused": one workgroup (256 or 1024 threads) scores a
+//   whole row and selects from LDS.  "parts": several 256-thread workgroups score slices of a
+//   row into the workspace and a second kernel (1024 threads per row) selects.  No workgroup
+//   ever waits on another inside a kernel.
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
@@ -33,59 +34,72 @@ namespace nosa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;          // sub-block groups per wave kept in flight
-constexpr int kRankMaxBlocks = 512; // rows up to this length use the one-pass rank selection
+constexpr int kUnroll = 4;           // groups of eight sub-blocks per wave kept in flight
+constexpr int kRankMaxBlocks = 512;  // rows up to this length use the one-pass rank selection
+constexpr int kCandMax = 512;        // candidates kept after the chunk-maximum bound
+constexpr int kEvPre = 4;            // eviction scores prefetched per thread
+constexpr int kKeyScratch = 256 + kCandMax;   // uint64 LDS entries of the top-k scratch
 
+template <int NT>
 struct SelectShared {
     uint32_t hist[256];
-    int scan[4];
+    int scan[NT / 64];
     int bcast[4];
 };
+
+// Inclusive sum over the NT threads of the workgroup, in thread order (all threads call it).
+template <int NT>
+__device__ __forceinline__ int block_incl_scan(int v, int *ws) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) ws[w] = v;
+    __syncthreads();
+    if (NW > 1 && w == 0) {
+        int t = lane < NW ? ws[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) {
+            const int u = __shfl_up(t, o, 64);
+            if (lane >= o) t += u;
+        }
+        if (lane < NW) ws[lane] = t;   // inclusive prefix of the wave totals
+    }
+    __syncthreads();
+    const int add = w > 0 ? ws[w - 1] : 0;
+    __syncthreads();
+    return v + add;
+}
 
 __device__ __forceinline__ uint64_t composite_key(uint32_t k, int id) {
     return ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-// Marks the kk best candidates (key descending, id ascending) in mark[0..n).
-// keybuf: LDS scratch of n uint64 (used by the rank path).
-template <class KeyF, class CandF>
-__device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, uint64_t *keybuf, SelectShared &sh) {
-    if (kk <= 0) return;
+// Radix select over 32-bit keys: marks the kk best candidates; equal keys go to the lowest ids.
+template <int NT, class KeyF, class CandF>
+__device__ void topk_radix(int n, int kk, KeyF key, CandF cand, uint8_t *mark, SelectShared<NT> &sh) {
     const int tid = threadIdx.x;
-    if (n <= kRankMaxBlocks) {
-        // rank of each candidate among all candidates; unique keys, non-candidates hold 0
-        for (int i = tid; i < n; i += kThreads) keybuf[i] = cand(i) ? composite_key(key(i), i) : 0ull;
-        __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
-            const uint64_t ki = keybuf[i];
-            if (ki == 0ull) continue;
-            int r = 0;
-            for (int j = 0; j < n; ++j) r += keybuf[j] > ki ? 1 : 0;
-            if (r < kk) mark[i] = 1;
-        }
-        __syncthreads();
-        return;
-    }
     uint32_t prefix = 0, pmask = 0;
     int need = kk;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        sh.hist[tid] = 0u;
+        if (tid < 256) sh.hist[tid] = 0u;
         if (tid == 0) { sh.bcast[0] = 0; sh.bcast[1] = 0; }
         __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
+        for (int i = tid; i < n; i += NT) {
             if (cand(i)) {
                 const uint32_t kv = key(i);
                 if ((kv & pmask) == prefix) atomicAdd(&sh.hist[(kv >> shift) & 255u], 1u);
             }
         }
         __syncthreads();
-        const int d = 255 - tid;
-        const int cnt = (int)sh.hist[d];
-        const int ge = block_incl_scan256(cnt, sh.scan);   // candidates with digit >= d
+        const int cnt = tid < 256 ? (int)sh.hist[255 - tid] : 0;
+        const int ge = block_incl_scan<NT>(cnt, sh.scan);   // candidates with digit >= 255 - tid
         const int gt = ge - cnt;
-        if (gt < need && need <= ge) { sh.bcast[0] = d; sh.bcast[1] = gt; }
+        if (tid < 256 && gt < need && need <= ge) { sh.bcast[0] = 255 - tid; sh.bcast[1] = gt; }
         __syncthreads();
         prefix |= (uint32_t)sh.bcast[0] << shift;
         pmask |= 0xFFu << shift;
@@ -94,12 +108,12 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
     }
     // prefix is the kk-th largest key; take every larger key and the `need` lowest ids equal to it.
     const uint32_t T = prefix;
-    const int per = (n + kThreads - 1) / kThreads;
+    const int per = (n + NT - 1) / NT;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int eq = 0;
     for (int i = lo; i < hi; ++i)
         if (cand(i) && key(i) == T) ++eq;
-    int rank = block_incl_scan256(eq, sh.scan) - eq;
+    int rank = block_incl_scan<NT>(eq, sh.scan) - eq;
     for (int i = lo; i < hi; ++i) {
         if (!cand(i)) continue;
         const uint32_t kv = key(i);
@@ -113,56 +127,196 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
     __syncthreads();
 }
 
-// Writes the ids i < n with flag(i) in ascending order to out[0..cap), padding with -1.
-template <class F>
-__device__ void compact_ids(int n, F flag, int32_t *out, int cap, SelectShared &sh) {
+// Marks the kk largest of the m unique keys buf[0..m) (zeros are empty slots): several lanes of a
+// wave count, for one key, the keys above it and add their counts with lane swaps, so a row of m
+// keys costs m * m / NT comparisons per thread.  mark_id(i, key, rank) is called for each winner.
+template <int NT, class MarkF>
+__device__ __forceinline__ void rank_mark(const uint64_t *buf, int m, int kk, MarkF mark_id) {
+    int tpc = 1;                                     // lanes per key: power of two, <= 64
+    while (tpc < 64 && tpc * 2 * m <= NT) tpc *= 2;
+    const int r = threadIdx.x & (tpc - 1);
+    for (int i = threadIdx.x / tpc; i < m; i += NT / tpc) {
+        const uint64_t ki = buf[i];
+        int cnt = 0;
+        int j = r;
+        for (; j + 7 * tpc < m; j += 8 * tpc) {   // eight independent LDS reads in flight
+            const uint64_t b0 = buf[j], b1 = buf[j + tpc], b2 = buf[j + 2 * tpc], b3 = buf[j + 3 * tpc];
+            const uint64_t b4 = buf[j + 4 * tpc], b5 = buf[j + 5 * tpc], b6 = buf[j + 6 * tpc], b7 = buf[j + 7 * tpc];
+            cnt += (b0 > ki) + (b1 > ki) + (b2 > ki) + (b3 > ki) + (b4 > ki) + (b5 > ki) + (b6 > ki) + (b7 > ki);
+        }
+        for (; j < m; j += tpc) cnt += buf[j] > ki ? 1 : 0;
+        for (int o = 1; o < tpc; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+        if (r == 0 && ki != 0ull && cnt < kk) mark_id(i, ki, cnt);
+    }
+}
+
+// Marks the kk best candidates (key descending, id ascending) in mark[0..n).  Keys are made
+// unique by appending the inverted block id (composite_key), so the kk-th best is well defined.
+//   n <= 512 : every candidate is ranked against all others (rank_mark).
+//   n  > 512 : the row is cut into 256 chunks; the kk-th best chunk maximum is a lower bound T0 of
+//              the kk-th best key overall (the kk best maxima are distinct keys >= T0), and at
+//              most kk chunks hold keys >= T0, so at most kk * chunk candidates survive; they are
+//              gathered and ranked.  When more than kCandMax survive, a radix select takes over.
+// keybuf: LDS scratch of 256 + kCandMax uint64.
+template <int NT, class KeyF, class CandF>
+__device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, uint64_t *keybuf, SelectShared<NT> &sh) {
+    if (kk <= 0) return;
     const int tid = threadIdx.x;
-    const int per = (n + kThreads - 1) / kThreads;
+    if (n <= kRankMaxBlocks) {
+        for (int i = tid; i < n; i += NT) keybuf[i] = cand(i) ? composite_key(key(i), i) : 0ull;
+        __syncthreads();
+        rank_mark<NT>(keybuf, n, kk, [&](int i, uint64_t, int) { mark[i] = 1; });
+        __syncthreads();
+        return;
+    }
+    constexpr int kChunks = 256;
+    constexpr int TPCH = NT / kChunks;              // threads per chunk (adjacent lanes)
+    uint64_t *tmax = keybuf;                        // [256] chunk maxima
+    uint64_t *cbuf = keybuf + kChunks;              // [kCandMax] surviving candidates
+    const int csize = (n + kChunks - 1) / kChunks;
+    {
+        const int ch = tid / TPCH, part = tid - ch * TPCH;
+        const int lo = min(n, ch * csize), hi = min(n, lo + csize);
+        uint64_t best = 0ull;
+        for (int i = lo + part; i < hi; i += TPCH)
+            if (cand(i)) {
+                const uint64_t c = composite_key(key(i), i);
+                best = c > best ? c : best;
+            }
+        for (int o = 1; o < TPCH; o <<= 1) {
+            const uint64_t other = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), o, 64) << 32) |
+                                   (uint32_t)__shfl_xor((int)(uint32_t)best, o, 64);
+            best = other > best ? other : best;
+        }
+        if (part == 0) tmax[ch] = best;
+        if (tid == 0) cbuf[0] = 1ull;   // T0 when fewer than kk chunks hold a candidate: keep all
+    }
+    __syncthreads();
+    // threshold T0: the kk-th best chunk maximum (the maximum ranked kk - 1)
+    rank_mark<NT>(tmax, kChunks, kk, [&](int, uint64_t ki, int rank) {
+        if (rank == kk - 1) cbuf[0] = ki;
+    });
+    __syncthreads();
+    const uint64_t T0 = cbuf[0];
+    __syncthreads();
+    const int per = (n + NT - 1) / NT;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int cnt = 0;
-    for (int i = lo; i < hi; ++i) cnt += flag(i) ? 1 : 0;
-    const int incl = block_incl_scan256(cnt, sh.scan);
-    int pos = incl - cnt;
     for (int i = lo; i < hi; ++i)
-        if (flag(i)) {
-            if (pos < cap) out[pos] = i;
-            ++pos;
+        if (cand(i) && composite_key(key(i), i) >= T0) ++cnt;
+    const int incl = block_incl_scan<NT>(cnt, sh.scan);
+    if (tid == NT - 1) sh.bcast[2] = incl;
+    __syncthreads();
+    const int total = sh.bcast[2];
+    if (total <= kCandMax) {
+        int pos = incl - cnt;
+        for (int i = lo; i < hi; ++i)
+            if (cand(i)) {
+                const uint64_t c = composite_key(key(i), i);
+                if (c >= T0) cbuf[pos++] = c;
+            }
+        __syncthreads();
+        rank_mark<NT>(cbuf, total, kk, [&](int, uint64_t c, int) { mark[0xFFFFFFFFu - (uint32_t)c] = 1; });
+        __syncthreads();
+        return;
+    }
+    topk_radix<NT>(n, kk, key, cand, mark, sh);
+}
+
+// Writes, in ascending id, the ids i < n with inE[i] to agn[0..ke) and those with inE[i] | inQ[i]
+// to sel[0..k), padding with -1: one scan over packed (agnostic, selected) counts.
+template <int NT>
+__device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, int32_t *agn, int ke, int32_t *sel,
+                                int k, SelectShared<NT> &sh) {
+    const int tid = threadIdx.x;
+    const int per = (n + NT - 1) / NT;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int cnt = 0;   // low 16 bits: selected; high 16 bits: agnostic
+    for (int i = lo; i < hi; ++i) cnt += ((inE[i] | inQ[i]) != 0 ? 1 : 0) + (inE[i] != 0 ? 0x10000 : 0);
+    const int incl = block_incl_scan<NT>(cnt, sh.scan);
+    int ps = (incl - cnt) & 0xFFFF, pe = (incl - cnt) >> 16;
+    for (int i = lo; i < hi; ++i) {
+        if (inE[i]) {
+            if (pe < ke) agn[pe] = i;
+            ++pe;
         }
-    if (tid == kThreads - 1) sh.bcast[2] = incl;
+        if (inE[i] | inQ[i]) {
+            if (ps < k) sel[ps] = i;
+            ++ps;
+        }
+    }
+    if (tid == NT - 1) sh.bcast[2] = incl;
     __syncthreads();
-    for (int p = sh.bcast[2] + tid; p < cap; p += kThreads) out[p] = -1;
-    __syncthreads();
+    const int ns = sh.bcast[2] & 0xFFFF, ne = sh.bcast[2] >> 16;
+    for (int p = ns + tid; p < k; p += NT) sel[p] = -1;
+    for (int p = ne + tid; p < ke; p += NT) agn[p] = -1;
 }
 
 // LDS layout of the selection phase for a row of n blocks.
 struct RowLds {
+    uint64_t *keys;     // [kKeyScratch] top-k scratch
     float *sc;          // [n] block scores
+    float *ev;          // [n] eviction scores, or nullptr (then read from global)
     uint8_t *inE;       // [n]
     uint8_t *inQ;       // [n]
-    uint64_t *keys;     // [n] (rank path, rows of up to kRankMaxBlocks blocks)
 };
 
+template <int NT>
+__host__ __device__ inline bool ev_in_lds(int n) { return n <= kEvPre * NT; }
+
+template <int NT>
 __host__ __device__ inline size_t row_lds_bytes(int n) {
     const size_t n16 = (size_t)((n + 15) & ~15);
-    return (n <= kRankMaxBlocks ? 8 * n16 : 0) + 4 * n16 + 2 * n16;
+    return 8 * (size_t)kKeyScratch + 4 * n16 + (ev_in_lds<NT>(n) ? 4 * n16 : 0) + 2 * n16;
 }
 
+template <int NT>
 __device__ inline RowLds carve(unsigned char *dyn, int n) {
     const int n16 = (n + 15) & ~15;
-    const int off = n <= kRankMaxBlocks ? 8 * n16 : 0;
     RowLds L;
-    L.keys = n <= kRankMaxBlocks ? (uint64_t *)dyn : nullptr;
-    L.sc = (float *)(dyn + off);
-    L.inE = dyn + off + 4 * n16;
-    L.inQ = L.inE + n16;
+    unsigned char *p = dyn;
+    L.keys = (uint64_t *)p;
+    p += 8 * kKeyScratch;
+    L.sc = (float *)p;
+    p += 4 * n16;
+    L.ev = nullptr;
+    if (ev_in_lds<NT>(n)) {
+        L.ev = (float *)p;
+        p += 4 * n16;
+    }
+    L.inE = p;
+    L.inQ = p + n16;
     return L;
 }
 
+// Loads up to kEvPre * NT eviction scores of the row into registers (issued early; stored to
+// LDS by ev_store once they are needed).
+template <int NT>
+__device__ __forceinline__ void ev_load(const SelectArgs &a, int row, float (&e)[kEvPre]) {
+    const float *evr = a.ev + (size_t)row * a.n_blocks_max;
+#pragma unroll
+    for (int r = 0; r < kEvPre; ++r) {
+        const int i = threadIdx.x + r * NT;
+        e[r] = i < a.n_blocks ? evr[i] : 0.0f;
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void ev_store(const RowLds &L, int n, const float (&e)[kEvPre]) {
+    if (!L.ev) return;
+#pragma unroll
+    for (int r = 0; r < kEvPre; ++r) {
+        const int i = threadIdx.x + r * NT;
+        if (i < n) L.ev[i] = e[r];
+    }
+}
+
 // Selection of one row from the block scores in L.sc (all threads of the workgroup).
-__device__ void select_row(const SelectArgs &a, int row, const RowLds &L, SelectShared &sh) {
+template <int NT>
+__device__ void select_row(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh) {
     const int tid = threadIdx.x;
     const int n = a.n_blocks;
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n; i += NT) {
         L.inE[i] = 0;
         L.inQ[i] = 0;
     }
@@ -172,79 +326,86 @@ __device__ void select_row(const SelectArgs &a, int row, const RowLds &L, Select
     const int n_prev = a.n_prev;
     const bool fresh = (n_prev == 0);
     if (!fresh)
-        for (int j = tid; j < a.ke; j += kThreads) {
+        for (int j = tid; j < a.ke; j += NT) {
             const int id = a.agn[(size_t)row * a.ke + j];
             if (id >= 0 && id < n_prev) L.inQ[id] = 1;   // previous Gamma_e (inQ reused as scratch)
         }
     __syncthreads();
-    const float *evr = a.ev + (size_t)row * a.n_blocks_max;
-    uint8_t *prevE = L.inQ;
-    topk_mark(
-        n, a.ke, [&](int i) { return order_key(evr[i]); },
+    const float *evg = a.ev + (size_t)row * a.n_blocks_max;
+    const float *evl = L.ev;
+    const uint8_t *prevE = L.inQ;
+    topk_mark<NT>(
+        n, a.ke, [&](int i) { return order_key(evl ? evl[i] : evg[i]); },
         [&](int i) { return fresh || prevE[i] || i >= n_prev; }, L.inE, L.keys, sh);
-    for (int i = tid; i < n; i += kThreads) L.inQ[i] = 0;
+    for (int i = tid; i < n; i += NT) L.inQ[i] = 0;
     __syncthreads();
 
     // Gamma_q: query-aware subset over the complement of Gamma_e
     const uint8_t *inE = L.inE;
     const float *sc = L.sc;
-    topk_mark(
+    topk_mark<NT>(
         n, a.kq, [&](int i) { return order_key(sc[i]); }, [&](int i) { return !inE[i]; }, L.inQ, L.keys, sh);
 
     // outputs, ascending block id
     const int k = a.kq + a.ke;
-    if (a.ke > 0) compact_ids(n, [&](int i) { return L.inE[i] != 0; }, a.agn + (size_t)row * a.ke, a.ke, sh);
-    compact_ids(n, [&](int i) { return (L.inE[i] | L.inQ[i]) != 0; }, a.sel + (size_t)row * k, k, sh);
+    compact_outputs<NT>(n, L.inE, L.inQ, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
+                        a.sel + (size_t)row * k, k, sh);
 }
 
-}  // namespace
-
-// Scores the blocks [part * blocks_per_part, ...) of one row; FUSED: the workgroup owns the whole
-// row, keeps the scores in LDS and selects.
-template <typename T, int D, int SPB, bool FUSED>
-__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
-    extern __shared__ __align__(16) unsigned char dyn[];
-    __shared__ __align__(16) float qs[D];
-    __shared__ SelectShared sh;
-
-    constexpr int CPLS = D / 32;   // 16-byte chunks per lane of one fp32 sub-block row
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int row = blockIdx.x / a.parts, part = blockIdx.x - row * a.parts;
-    const int b = row / a.Hkv, g = row - b * a.Hkv;
-    const int n = a.n_blocks;
-    RowLds L;
-    if (FUSED) L = carve(dyn, n);
-
-    for (int c = tid; c < D; c += kThreads) {
-        float s = 0.0f;
-        for (int h = 0; h < a.G; ++h) s += load_elem<T>(a.q, ((size_t)(b * a.Hq + g * a.G + h)) * D + c);
-        qs[c] = s;
-    }
-    __syncthreads();
-
-    const int r8 = lane >> 3, c8 = lane & 7;
-    float4 qv[CPLS];
+// qs slice of this lane: float4 chunks c8 + 8 i of sum_h q[b][g*G + h].
+template <typename T, int D>
+__device__ __forceinline__ void group_query(const SelectArgs &a, int b, int g, int c8, float4 (&qv)[D / 32]) {
 #pragma unroll
-    for (int i = 0; i < CPLS; ++i) qv[i] = *(const float4 *)&qs[(c8 + 8 * i) * 4];
-    const int blk_lo = part * a.blocks_per_part;
-    const int blk_hi = min(n, blk_lo + a.blocks_per_part);
+    for (int i = 0; i < D / 32; ++i) qv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h = 0; h < a.G; ++h) {
+        const size_t base = (size_t)(b * a.Hq + g * a.G + h) * D;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const size_t e0 = base + (size_t)(c8 + 8 * i) * 4;
+            if (sizeof(T) == 2) {
+                const uint2 u = *(const uint2 *)((const uint16_t *)a.q + e0);
+                qv[i].x += bf16_lo(u.x);
+                qv[i].y += bf16_hi(u.x);
+                qv[i].z += bf16_lo(u.y);
+                qv[i].w += bf16_hi(u.y);
+            } else {
+                const float4 f = *(const float4 *)((const float *)a.q + e0);
+                qv[i].x += f.x;
+                qv[i].y += f.y;
+                qv[i].z += f.z;
+                qv[i].w += f.w;
+            }
+        }
+    }
+}
+
+// Scores blocks [blk_lo, blk_hi) of one row; writes them to LDS (sc) or global (gscore).
+template <typename T, int D, int SPB, int NT>
+__device__ __forceinline__ void score_range(const SelectArgs &a, int row, int blk_lo, int blk_hi, float *sc,
+                                            float *gscore) {
+    constexpr int CPLS = D / 32;   // 16-byte chunks per lane of one fp32 sub-block row
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
+    const int r8 = lane >> 3, c8 = lane & 7;
     const int sb_lo = blk_lo * SPB, sb_hi = blk_hi * SPB;
     const int ngroups = (sb_hi - sb_lo + 7) >> 3;   // groups of 8 sub-blocks
     const float *kprow = a.kp + (size_t)row * a.n_blocks_max * SPB * D;
-    float *gscore = a.scores + (size_t)row * a.scores_stride;
-    for (int g0 = w; g0 < ngroups; g0 += 4 * kUnroll) {
+    float4 qv[CPLS];
+    group_query<T, D>(a, b, g, c8, qv);
+    for (int g0 = w; g0 < ngroups; g0 += NW * kUnroll) {
         float4 x[kUnroll][CPLS];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int j = sb_lo + (g0 + 4 * u) * 8 + r8;
-            const bool v = (g0 + 4 * u < ngroups) && (j < sb_hi);
+            const int j = sb_lo + (g0 + NW * u) * 8 + r8;
+            const bool v = (g0 + NW * u < ngroups) && (j < sb_hi);
 #pragma unroll
             for (int i = 0; i < CPLS; ++i)
                 x[u][i] = v ? *(const float4 *)(kprow + (size_t)j * D + (c8 + 8 * i) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int j = sb_lo + (g0 + 4 * u) * 8 + r8;
+            const int j = sb_lo + (g0 + NW * u) * 8 + r8;
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPLS; ++i) {
@@ -259,32 +420,59 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
             if (SPB >= 2) s = fmaxf(s, dpp<kDppRowMirror>(s));
             if (SPB >= 4) s = fmaxf(s, xor_lane(s, 16));
             if (SPB >= 8) s = fmaxf(s, xor_lane(s, 32));
-            const bool v = (g0 + 4 * u < ngroups) && (j < sb_hi);
+            const bool v = (g0 + NW * u < ngroups) && (j < sb_hi);
             if (v && (lane % (8 * SPB)) == 0) {
                 const int blk = j / SPB;
-                if (FUSED) L.sc[blk] = s;
+                if (sc) sc[blk] = s;
                 else gscore[blk] = s;
             }
         }
     }
-    if (!FUSED) return;
-    __syncthreads();
-    select_row(a, row, L, sh);
 }
 
-// Selection of rows scored by score_kernel<..., false>: one workgroup per row.
-__global__ __launch_bounds__(256) void pick_kernel(SelectArgs a) {
+}  // namespace
+
+// One workgroup scores a whole row, keeps the scores in LDS and selects.
+template <typename T, int D, int SPB, int NT>
+__global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char dyn[];
-    __shared__ SelectShared sh;
+    __shared__ SelectShared<NT> sh;
     const int row = blockIdx.x;
-    const RowLds L = carve(dyn, a.n_blocks);
-    const float *gscore = a.scores + (size_t)row * a.scores_stride;
-    for (int i = threadIdx.x; i < a.n_blocks; i += kThreads) L.sc[i] = gscore[i];
+    const RowLds L = carve<NT>(dyn, a.n_blocks);
+    float e[kEvPre];
+    ev_load<NT>(a, row, e);
+    score_range<T, D, SPB, NT>(a, row, 0, a.n_blocks, L.sc, nullptr);
+    ev_store<NT>(L, a.n_blocks, e);
     __syncthreads();
-    select_row(a, row, L, sh);
+    select_row<NT>(a, row, L, sh);
 }
 
-size_t select_lds_bytes(int n_blocks) { return row_lds_bytes(n_blocks); }
+// A slice of a row's blocks, scored into the global score buffer.
+template <typename T, int D, int SPB>
+__global__ __launch_bounds__(256) void score_part_kernel(SelectArgs a) {
+    const int row = blockIdx.x / a.parts, part = blockIdx.x - row * a.parts;
+    const int blk_lo = part * a.blocks_per_part;
+    const int blk_hi = min(a.n_blocks, blk_lo + a.blocks_per_part);
+    score_range<T, D, SPB, 256>(a, row, blk_lo, blk_hi, nullptr, a.scores + (size_t)row * a.scores_stride);
+}
+
+// Selection of rows scored by score_part_kernel: one workgroup per row.
+template <int NT>
+__global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ SelectShared<NT> sh;
+    const int row = blockIdx.x;
+    const RowLds L = carve<NT>(dyn, a.n_blocks);
+    float e[kEvPre];
+    ev_load<NT>(a, row, e);
+    const float *gscore = a.scores + (size_t)row * a.scores_stride;
+    for (int i = threadIdx.x; i < a.n_blocks; i += NT) L.sc[i] = gscore[i];
+    ev_store<NT>(L, a.n_blocks, e);
+    __syncthreads();
+    select_row<NT>(a, row, L, sh);
+}
+
+size_t select_lds_bytes(int n_blocks) { return row_lds_bytes<1024>(n_blocks); }
 
 template <class K>
 static hipError_t allow_lds(K kern, size_t dyn) {
@@ -293,36 +481,47 @@ static hipError_t allow_lds(K kern, size_t dyn) {
 }
 
 template <typename T, int D, int SPB>
-static hipError_t launch_select_t(const SelectArgs &a, int rows, hipStream_t st) {
+static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threads, hipStream_t st) {
     hipError_t e;
     if (a.parts == 1 && !a.scores_only) {
-        const size_t dyn = row_lds_bytes(a.n_blocks);
-        auto kern = score_kernel<T, D, SPB, true>;
-        if ((e = allow_lds(kern, dyn)) != hipSuccess) return e;
-        kern<<<dim3((unsigned)rows), dim3(kThreads), dyn, st>>>(a);
+        if (fused_threads == 1024) {
+            const size_t dyn = row_lds_bytes<1024>(a.n_blocks);
+            auto kern = score_select_kernel<T, D, SPB, 1024>;
+            if ((e = allow_lds(kern, dyn)) != hipSuccess) return e;
+            kern<<<dim3((unsigned)rows), dim3(1024), dyn, st>>>(a);
+        } else {
+            const size_t dyn = row_lds_bytes<256>(a.n_blocks);
+            auto kern = score_select_kernel<T, D, SPB, 256>;
+            if ((e = allow_lds(kern, dyn)) != hipSuccess) return e;
+            kern<<<dim3((unsigned)rows), dim3(256), dyn, st>>>(a);
+        }
         return hipGetLastError();
     }
-    score_kernel<T, D, SPB, false><<<dim3((unsigned)(rows * a.parts)), dim3(kThreads), 0, st>>>(a);
+    score_part_kernel<T, D, SPB><<<dim3((unsigned)(rows * a.parts)), dim3(256), 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess || a.scores_only) return e;
-    const size_t dyn = row_lds_bytes(a.n_blocks);
-    if ((e = allow_lds(pick_kernel, dyn)) != hipSuccess) return e;
-    pick_kernel<<<dim3((unsigned)rows), dim3(kThreads), dyn, st>>>(a);
+    const size_t dyn = row_lds_bytes<1024>(a.n_blocks);
+    if ((e = allow_lds(pick_kernel<1024>, dyn)) != hipSuccess) return e;
+    pick_kernel<1024><<<dim3((unsigned)rows), dim3(1024), dyn, st>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_select_d(int spb, const SelectArgs &a, int rows, hipStream_t st) {
+static hipError_t launch_select_d(int spb, const SelectArgs &a, int rows, int fused_threads, hipStream_t st) {
     switch (spb) {
-        case 1: return launch_select_t<T, D, 1>(a, rows, st);
-        case 2: return launch_select_t<T, D, 2>(a, rows, st);
-        case 4: return launch_select_t<T, D, 4>(a, rows, st);
-        default: return launch_select_t<T, D, 8>(a, rows, st);
+        case 1: return launch_select_t<T, D, 1>(a, rows, fused_threads, st);
+        case 2: return launch_select_t<T, D, 2>(a, rows, fused_threads, st);
+        case 4: return launch_select_t<T, D, 4>(a, rows, fused_threads, st);
+        default: return launch_select_t<T, D, 8>(a, rows, fused_threads, st);
     }
 }
 
-hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, hipStream_t st) {
-    if (dtype == 1) return d == 128 ? launch_select_d<uint16_t, 128>(spb, a, rows, st) : launch_select_d<uint16_t, 64>(spb, a, rows, st);
-    return d == 128 ? launch_select_d<float, 128>(spb, a, rows, st) : launch_select_d<float, 64>(spb, a, rows, st);
+hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads,
+                         hipStream_t st) {
+    if (dtype == 1)
+        return d == 128 ? launch_select_d<uint16_t, 128>(spb, a, rows, fused_threads, st)
+                        : launch_select_d<uint16_t, 64>(spb, a, rows, fused_threads, st);
+    return d == 128 ? launch_select_d<float, 128>(spb, a, rows, fused_threads, st)
+                    : launch_select_d<float, 64>(spb, a, rows, fused_threads, st);
 }
 
 }  // namespace nosa

@@ -76,7 +76,7 @@ def test_select(name, parts):
     sel, agn = H.gpu_select(shape, q_dev, kp_dev, H.dev(x["evict"]), ws)
     s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], sbs), w.n_blocks, 64 // sbs)
     H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"][:, :, :w.n_blocks], w.kq, w.ke)
-    # repeat: bitwise identical (deterministic, workspace counters reset)
+    # repeat: bitwise identical (deterministic)
     sel2, agn2 = H.gpu_select(shape, q_dev, kp_dev, H.dev(x["evict"]), ws)
     assert torch.equal(sel, sel2) and torch.equal(agn, agn2)
 
@@ -256,3 +256,59 @@ def test_c1_tiny_end_to_end():
     out = H.gpu_decode(shape, q_dev, H.dev(x["k"]), H.dev(x["v"]), w.nbmax, sel, ws)
     ref = O.attention(x["q"], x["k"], x["v"], H.host(sel).reshape(1, 1, -1))
     H.check_attention(H.host(out), ref, "f32", "C1")
+
+
+@pytest.mark.parametrize("n,kq,ke,parts", [(513, 16, 16, 0), (1300, 40, 24, 3), (1300, 40, 24, 1), (2048, 32, 32, 0),
+                                           (5000, 32, 32, 7), (700, 300, 100, 0), (4100, 20, 30, 1)])
+def test_select_long_rows(n, kq, ke, parts):
+    # Rows longer than 512 blocks take the bounded-candidate top-k; the next step (blocks arrive,
+    # strict eviction) runs the same path with few query-agnostic candidates.
+    rng = np.random.default_rng(n)
+    B, Hkv, G, d = 2, 2, 4, 128
+    nbmax = n + 9
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    kp = rng.standard_normal((B, Hkv, nbmax * 2, d)).astype(np.float32)
+    ev = rng.random((B, Hkv, nbmax), dtype=np.float32)
+    shape = N.make_shape(batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=d, n_blocks=n, n_blocks_max=nbmax,
+                         kq=kq, ke=ke, dtype=N.NOSA_F32, select_parts=parts)
+    ws = N.workspace(shape)
+    q_dev, kp_dev, ev_dev = H.dev(q), H.dev(kp), H.dev(ev)
+    sel, agn = H.gpu_select(shape, q_dev, kp_dev, ev_dev, ws)
+    s_ref = O.block_scores(q, kp.astype(np.float64)[:, :, :2 * n], n, 2)
+    H.check_selection(H.host(sel), H.host(agn), s_ref, ev, kq, ke)
+    _, agn_ref, _ = O.select(s_ref, ev, kq, ke)
+    n2 = n + 9
+    shape2 = shape.copy(n_blocks=n2)
+    sel2, agn2 = H.gpu_select(shape2, q_dev, kp_dev, ev_dev, ws, n_prev=n, agn=agn)
+    s_ref2 = O.block_scores(q, kp.astype(np.float64), n2, 2)
+    H.check_selection(H.host(sel2), H.host(agn2), s_ref2, ev, kq, ke, n, agn_ref)
+
+
+def test_select_long_rows_all_ties():
+    # Equal scores everywhere: the winners are the lowest ids.  At 16384 blocks the chunk-maximum
+    # bound leaves too many candidates, so this also runs the radix-select fallback.
+    B, Hkv, G, d, n, kq, ke = 1, 2, 4, 64, 16384, 32, 32
+    shape = N.make_shape(batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=d, n_blocks=n, kq=kq, ke=ke,
+                         dtype=N.NOSA_BF16)
+    q = torch.ones((B, Hkv * G, d), dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros((B * Hkv, n * 2, d), dtype=torch.float32, device="cuda")
+    ev = torch.full((B, Hkv, n), 0.25, dtype=torch.float32, device="cuda")
+    sel, agn = H.gpu_select(shape, q, kp, ev, N.workspace(shape))
+    assert H.host(agn).tolist() == [list(range(ke))] * 2
+    assert H.host(sel).tolist() == [list(range(kq + ke))] * 2
+
+
+def test_select_many_rows_one_workgroup_each():
+    # 256 rows: the plan gives every row its own 256-thread workgroup that scores and selects.
+    w = small_workload("wide", batch=64, n_q_heads=16, n_kv_heads=4, head_dim=64, n_blocks=20, kq=3, ke=5, seed=36)
+    x = generate(w)
+    shape = H.shape_of(w)
+    q_dev = H.dev(x["q"])
+    kp = H.gpu_pool(shape, H.dev(x["k"]))
+    ws = N.workspace(shape)
+    sel, agn = H.gpu_select(shape, q_dev, kp, H.dev(x["evict"]), ws)
+    s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], 32), w.n_blocks, 2)
+    H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke)
+    out = H.gpu_decode(shape, q_dev, H.dev(x["k"]), H.dev(x["v"]), w.nbmax, sel, ws)
+    ref = O.attention(x["q"], x["k"], x["v"], H.host(sel).reshape(w.batch, w.n_kv_heads, w.k))
+    H.check_attention(H.host(out), ref, "bf16", "wide")

@@ -378,3 +378,18 @@ def test_attention_dominant_token_returns_its_value():
 def test_locality_hand_example():
     g = O.locality(np.array([[0, 2, 5, 7]], np.int32), np.array([[2, 3, 5, 9]], np.int32), 10)
     assert g.tolist() == [0.5]
+
+
+def test_c1_regression_record():
+    # The oracle still reproduces its recorded C1 result (tests/golden/make_golden.py).
+    import json
+    import os
+    from nosa_inputs import WORKLOADS
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "c1_oracle.json")))
+    w = WORKLOADS["C1"]
+    x = generate(w)
+    r = O.decode_step(x["q"], O.pool_keys(x["k"], 32), x["evict"], x["k"], x["v"], w.n_blocks, w.kq, w.ke, 2)
+    assert r["selected"].reshape(-1).tolist() == rec["selected"]
+    assert r["agn_state"].reshape(-1).tolist() == rec["agn_state"]
+    np.testing.assert_allclose(r["scores"].reshape(-1), rec["block_scores"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["out"].reshape(-1), rec["out"], rtol=1e-12, atol=1e-12)
