@@ -40,13 +40,17 @@ _INPUTS = {}
 
 
 def inputs(cfg):
-    """Generated host inputs of a workload, drawn once per process."""
+    """Generated host inputs of a workload, drawn once per process (workloads that draw the same
+    tensors, e.g. a different budget split on the same seed, share them)."""
     from nosa_inputs import WORKLOADS, generate
-    if cfg not in _INPUTS:
+    w = WORKLOADS[cfg]
+    key = (w.seed, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.nbmax, w.dtype, w.block_offset_sigma,
+           w.steps, w.drift_sigma)
+    if key not in _INPUTS:
         t0 = time.time()
-        _INPUTS[cfg] = generate(WORKLOADS[cfg])
+        _INPUTS[key] = generate(w)
         log("[bench] %s inputs generated in %.1fs" % (cfg, time.time() - t0))
-    return _INPUTS[cfg]
+    return _INPUTS[key]
 
 
 def algorithmic_bytes(w):
@@ -83,7 +87,7 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
     shape = N.make_shape(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                          n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, sub_block_size=32,
                          dtype=N.NOSA_BF16 if w.dtype == "bf16" else N.NOSA_F32, decode_splits=decode_splits,
-                         select_parts=select_parts)
+                         select_parts=select_parts, sink_blocks=w.n_sink, window_blocks=w.n_window)
     q, k, v, ev = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["evict"])
     R = w.rows
     kp = torch.empty((R, w.nbmax * 2, w.head_dim), dtype=torch.float32, device="cuda")
@@ -259,7 +263,8 @@ def cpu_baseline(cfg, budget_s=10.0, max_s=30.0):
     kp = O.pool_keys(x["k"], 32)      # state, excluded like on the GPU
     reps, t0 = 0, time.perf_counter()
     while True:
-        O.decode_step(x["q"], kp, x["evict"], x["k"], x["v"], w.n_blocks, w.kq, w.ke, 2)
+        O.decode_step(x["q"], kp, x["evict"], x["k"], x["v"], w.n_blocks, w.kq, w.ke, 2, n_sink=w.n_sink,
+                      n_window=w.n_window)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or el + el / reps > max_s:
@@ -282,8 +287,11 @@ def traffic_record():
 
 
 def describe(w):
-    return "%s: B%d, GQA %d/%d, d%d, ctx %d, budget %d+%d blocks of 64 tokens, %s" % (
-        w.name, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.kq, w.ke, w.dtype)
+    extra = ""
+    if w.n_sink or w.n_window:
+        extra = " (agnostic part incl. %d sink + %d window blocks)" % (w.n_sink, w.n_window)
+    return "%s: B%d, GQA %d/%d, d%d, ctx %d, budget %d+%d blocks of 64 tokens%s, %s" % (
+        w.name, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.kq, w.ke, extra, w.dtype)
 
 
 def main():
@@ -292,7 +300,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C2")
-    ap.add_argument("--also", default="C3", help="comma list of extra resident workloads ('' for none)")
+    ap.add_argument("--also", default="C3,F1", help="comma list of extra resident workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--offload", action="store_true", help="also run the 128-step offload loop")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -13,7 +13,8 @@ import os
 from typing import Any, Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnosa.so")
+# NOSA_LIBRARY selects another build of the same library (e.g. an experimental variant).
+LIB_PATH = os.environ.get("NOSA_LIBRARY") or os.path.join(_PKG, "libnosa.so")
 
 NOSA_OK, NOSA_EINVAL, NOSA_EUNSUPPORTED, NOSA_ECAPACITY, NOSA_EHIP = 0, -1, -2, -3, -4
 NOSA_F32, NOSA_BF16 = 0, 1
@@ -34,7 +35,8 @@ class NosaShape(ctypes.Structure):
     """Mirror of ``nosa_shape``."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "block_size", "sub_block_size", "n_blocks",
-        "n_blocks_max", "kq", "ke", "cache_slots", "dtype", "decode_splits", "select_parts")]
+        "n_blocks_max", "kq", "ke", "cache_slots", "dtype", "decode_splits", "select_parts", "sink_blocks",
+        "window_blocks")]
 
     def copy(self, **changes) -> "NosaShape":
         s = NosaShape()
@@ -49,13 +51,14 @@ class NosaShape(ctypes.Structure):
 
 def make_shape(*, batch, n_q_heads, n_kv_heads, head_dim, n_blocks, kq, ke, n_blocks_max=None,
                block_size=64, sub_block_size=32, cache_slots=0, dtype=NOSA_BF16, decode_splits=0,
-               select_parts=0) -> NosaShape:
+               select_parts=0, sink_blocks=0, window_blocks=0) -> NosaShape:
     s = NosaShape()
     s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim = batch, n_q_heads, n_kv_heads, head_dim
     s.block_size, s.sub_block_size, s.n_blocks = block_size, sub_block_size, n_blocks
     s.n_blocks_max = n_blocks if n_blocks_max is None else n_blocks_max
     s.kq, s.ke, s.cache_slots, s.dtype = kq, ke, cache_slots, dtype
     s.decode_splits, s.select_parts = decode_splits, select_parts
+    s.sink_blocks, s.window_blocks = sink_blocks, window_blocks
     return s
 
 

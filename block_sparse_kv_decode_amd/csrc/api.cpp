@@ -76,6 +76,11 @@ int check_shape(const nosa_shape *s) {
         return fail(NOSA_EINVAL, "budget kq + ke = %d exceeds the %d visible blocks", s->kq + s->ke, s->n_blocks);
     if (s->decode_splits < 0 || s->select_parts < 0)
         return fail(NOSA_EINVAL, "decode_splits and select_parts must be >= 0");
+    if (s->sink_blocks < 0 || s->window_blocks < 0 || s->sink_blocks + s->window_blocks > s->ke)
+        return fail(NOSA_EINVAL, "sink_blocks (%d) and window_blocks (%d) must be >= 0 and fit in ke (%d)",
+                    s->sink_blocks, s->window_blocks, s->ke);
+    if (s->n_blocks < s->sink_blocks + s->window_blocks)
+        return fail(NOSA_EINVAL, "n_blocks %d is below sink_blocks + window_blocks", s->n_blocks);
     return NOSA_OK;
 }
 
@@ -234,6 +239,8 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
         if (shape->ke > 0) REQUIRE_PTR(agn_state, 4);
         if (n_prev < 0 || n_prev > shape->n_blocks)
             return fail(NOSA_EINVAL, "n_blocks_prev %d must lie in [0, n_blocks=%d]", n_prev, shape->n_blocks);
+        if (n_prev > 0 && n_prev < shape->sink_blocks + shape->window_blocks)
+            return fail(NOSA_EINVAL, "n_blocks_prev %d is below sink_blocks + window_blocks", n_prev);
     }
     const WsLayout L = ws_layout(shape);
     const PartPlan pp = select_plan(shape);
@@ -252,6 +259,8 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
     a.kq = shape->kq;
     a.ke = shape->ke;
     a.n_prev = n_prev;
+    a.n_sink = shape->sink_blocks;
+    a.n_window = shape->window_blocks;
     a.parts = pp.P;
     a.blocks_per_part = pp.bpp;
     a.scores_only = scores_only ? 1 : 0;

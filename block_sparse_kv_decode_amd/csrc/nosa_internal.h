@@ -30,6 +30,7 @@ struct SelectArgs {
     float *scores;        // [R, scores_stride] global block scores (parts > 1, or scores-only mode)
     int Hq, Hkv, G;
     int n_blocks, n_blocks_max, kq, ke, n_prev;
+    int n_sink, n_window;  // blocks always in the query-agnostic subset (start / end of the context)
     int parts;            // workgroups per row
     int blocks_per_part;
     int scores_only;      // 1: stop after writing block scores

@@ -15,8 +15,9 @@
 //   lane group and load), reduce with three DPP adds and max-pool the block's sub-blocks with DPP
 //   and lane swaps; each wave keeps four groups of eight rows in flight.
 // Selection (one workgroup per row, in LDS).
-//   Gamma_e: top-ke by eviction score among all visible blocks (first step) or among the
-//            previous Gamma_e plus the newly visible blocks (strict eviction);
+//   Gamma_e: the sink and window blocks (if any), plus the best blocks by eviction score among
+//            all other visible blocks (first step) or among the previous score-ranked members
+//            and the blocks that left the window since (strict eviction);
 //   Gamma_q: top-kq by block score among the visible blocks outside Gamma_e.
 //   Exact top-k on unique 64-bit keys (order-preserving score bits, then the inverted block id,
 //   so equal scores go to the lower id): rows of up to 512 blocks rank every candidate against
@@ -322,21 +323,26 @@ __device__ void select_row(const SelectArgs &a, int row, const RowLds &L, Select
     }
     __syncthreads();
 
-    // Gamma_e: query-agnostic subset under strict eviction
+    // Gamma_e: sink and window blocks, plus the score-ranked members under strict eviction
     const int n_prev = a.n_prev;
     const bool fresh = (n_prev == 0);
+    const int w_lo = n - a.n_window;              // first window block
+    const int left = n_prev - a.n_window;         // blocks below this were ranked (or out) last step
     if (!fresh)
         for (int j = tid; j < a.ke; j += NT) {
             const int id = a.agn[(size_t)row * a.ke + j];
             if (id >= 0 && id < n_prev) L.inQ[id] = 1;   // previous Gamma_e (inQ reused as scratch)
         }
+    for (int i = tid; i < n; i += NT)
+        if (i < a.n_sink || i >= w_lo) L.inE[i] = 1;
     __syncthreads();
     const float *evg = a.ev + (size_t)row * a.n_blocks_max;
     const float *evl = L.ev;
     const uint8_t *prevE = L.inQ;
+    const int n_sink = a.n_sink;
     topk_mark<NT>(
-        n, a.ke, [&](int i) { return order_key(evl ? evl[i] : evg[i]); },
-        [&](int i) { return fresh || prevE[i] || i >= n_prev; }, L.inE, L.keys, sh);
+        n, a.ke - a.n_sink - a.n_window, [&](int i) { return order_key(evl ? evl[i] : evg[i]); },
+        [&](int i) { return i >= n_sink && i < w_lo && (fresh || i >= left || prevE[i]); }, L.inE, L.keys, sh);
     for (int i = tid; i < n; i += NT) L.inQ[i] = 0;
     __syncthreads();
 

@@ -73,6 +73,8 @@ typedef struct {
     int32_t dtype;           /* nosa_dtype of q, K, V, output */
     int32_t decode_splits;   /* split-K partitions per row in nosa_sparse_decode; 0 = automatic */
     int32_t select_parts;    /* workgroups that score one row in nosa_select; 0 = automatic */
+    int32_t sink_blocks;     /* first blocks always in the query-agnostic subset (0 = none) */
+    int32_t window_blocks;   /* most recent visible blocks always in it (0 = none) */
 } nosa_shape;
 
 /* Message for the last failed call on this thread ("" if none).  Never NULL. */
@@ -116,15 +118,20 @@ int nosa_block_scores(const nosa_shape *shape, const void *q, const float *poole
 /*
  * Block selection for one decode step ([P1] §2.1, §3.1, App. A, App. E; [P4] Method 1).
  * Per row, with the block scores s of nosa_block_scores and the fixed per-block eviction scores e:
- *   Query-agnostic subset Gamma_e (ke blocks, highest e first):
- *     n_blocks_prev == 0 : chosen among all visible blocks [0, n_blocks)  (first step).
- *     n_blocks_prev  > 0 : chosen among Gamma_e of the previous step (agn_state on entry) and the
- *                          blocks [n_blocks_prev, n_blocks) that became visible since then.  A block
- *                          once left out of Gamma_e never re-enters it (strict eviction), so
- *                          consecutive selections share at least ke - (admitted arrivals) blocks.
+ *   Query-agnostic subset Gamma_e (ke blocks).  The sink_blocks first blocks and the window_blocks
+ *   last visible blocks always belong to it ([P1] B.2.2: the paper's query-agnostic blocks include an
+ *   attention sink and a sliding window); the other ke - sink - window members are the blocks with
+ *   the highest e among the candidates:
+ *     n_blocks_prev == 0 : all visible blocks outside sink and window (first step).
+ *     n_blocks_prev  > 0 : the previous score-ranked members (from agn_state on entry) and the
+ *                          blocks that left the window, or became visible past it, since then
+ *                          ([n_blocks_prev - window, n_blocks - window)).  A block once left out
+ *                          of Gamma_e never re-enters it (strict eviction), so consecutive
+ *                          selections share at least ke - (blocks that became visible) blocks.
  *   Query-aware subset Gamma_q: the kq visible blocks outside Gamma_e with the highest s.
  *   Ties on e or s go to the lower block id.  The selection is Gamma_e U Gamma_q, k = kq + ke
- *   distinct blocks, written in ascending block id.
+ *   distinct blocks, written in ascending block id.  Requires sink + window <= ke,
+ *   n_blocks >= sink + window, and n_blocks_prev == 0 or n_blocks_prev >= sink + window.
  *   q           : device, [B, Hq, d], dtype
  *   pooled_k    : device, [B, Hkv, n_blocks_max * spb, d] float32 (nosa_pool_keys)
  *   evict       : device, [B, Hkv, n_blocks_max] float32, first n_blocks used; finite values

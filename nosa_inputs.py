@@ -71,6 +71,8 @@ class Workload:
     cache_slots: int = 0              # GPU cache slots per KV head (offload loop only)
     steps: int = 1                    # decode steps (offload loop only)
     drift_sigma: float = 0.0          # std of the per-step query drift (offload loop only)
+    n_sink: int = 0                   # first blocks always in the query-agnostic subset
+    n_window: int = 0                 # most recent blocks always in the query-agnostic subset
     description: str = ""
 
     @property
@@ -103,16 +105,22 @@ WORKLOADS: Dict[str, Workload] = {
                    description="offload loop: C2 shape, 128 steps, 64-slot GPU cache, pinned host pool"),
     "C5": Workload("C5", 4, 32, 8, 128, 131072, 32, 32, "bf16", seed=5,
                    description="long context: B4, GQA 32/8, d128, 128K ctx, 32+32 blocks, bf16"),
+    # The paper's own budget split on the C2 tensors (same seed): 16 query-aware blocks and 48
+    # query-agnostic ones that include 1 sink block and a 16-block sliding window.
+    "F1": Workload("F1", 16, 32, 8, 128, 16384, 16, 48, "bf16", seed=2, n_sink=1, n_window=16,
+                   description="C2 tensors with the paper split: 16 query-aware + 48 agnostic (1 sink, 16 window)"),
 }
 
 
 def small_workload(name: str = "small", *, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
                    n_blocks=37, kq=5, ke=7, dtype="bf16", seed=11, n_blocks_max=None,
-                   cache_slots=0, steps=1, drift_sigma=0.0, block_offset_sigma=0.5) -> Workload:
+                   cache_slots=0, steps=1, drift_sigma=0.0, block_offset_sigma=0.5, n_sink=0,
+                   n_window=0) -> Workload:
     """A reduced workload with the same generator, for tests the oracle finishes in seconds."""
     return Workload(name, batch, n_q_heads, n_kv_heads, head_dim, n_blocks * BLOCK, kq, ke, dtype,
                     seed=seed, block_offset_sigma=block_offset_sigma, n_blocks_max=n_blocks_max,
-                    cache_slots=cache_slots, steps=steps, drift_sigma=drift_sigma)
+                    cache_slots=cache_slots, steps=steps, drift_sigma=drift_sigma, n_sink=n_sink,
+                    n_window=n_window)
 
 
 def _round(x: np.ndarray, dtype: str) -> np.ndarray:

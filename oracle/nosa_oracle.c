@@ -166,12 +166,17 @@ static int topk_plain(int n, const double *key, const uint8_t *cand, int kk, uin
  * Block selection for one decode step.
  *
  * Query-agnostic subset Gamma_e ([P1] §2.1 and §1; [P4] Method 1, dual selection with
- * strict eviction): ke blocks ranked by their fixed eviction score e.  Strict eviction:
- * a block that is not in Gamma_e at some step never enters Gamma_e again.
- *   - n_prev == 0 (first step): candidates are all visible blocks [0, n_blocks).
- *   - otherwise: candidates are Gamma_e(t-1) (read from agn_state) and the blocks that
- *     became visible since the previous step, [n_prev, n_blocks).  Every other block was
- *     left out at an earlier step and stays out.
+ * strict eviction): ke blocks.  Optionally ([P1] B.2.2: the query-agnostic blocks of the
+ * paper's setting include one attention-sink block and a sliding window of recent blocks)
+ * the first n_sink blocks and the last n_window visible blocks always belong to Gamma_e;
+ * the other ke - n_sink - n_window members are ranked by the fixed eviction score e under
+ * strict eviction: a block that is not in Gamma_e at some step never enters it again.
+ *   - n_prev == 0 (first step): candidates are all visible blocks outside sink and window.
+ *   - otherwise: candidates are the previous score-ranked members (blocks of Gamma_e(t-1)
+ *     that were neither sink nor window then, i.e. below n_prev - n_window) and the blocks
+ *     that left the window (or became visible past it) since the previous step,
+ *     [n_prev - n_window, n_blocks - n_window).  Every other block was left out at an
+ *     earlier step and stays out.
  * Query-aware subset Gamma_q ([P1] §2.1 and App. A; [P4] Method 1): the kq blocks with the
  * highest block score s among the visible blocks outside Gamma_e, so Gamma_e and Gamma_q
  * are disjoint and the selection holds exactly k = kq + ke blocks (reading: Gamma_e is
@@ -182,43 +187,57 @@ static int topk_plain(int n, const double *key, const uint8_t *cand, int kk, uin
  *   agn_state : [R][ke] int32  in: Gamma_e(t-1) (ignored when n_prev == 0); out: Gamma_e(t), ascending
  *   selected  : [R][kq+ke] int32 out: Gamma_e(t) U Gamma_q(t), ascending
  *   is_agn    : [R][kq+ke] uint8 out (may be NULL): 1 where selected[i] came from Gamma_e
+ * Requires n_sink + n_window <= ke, n_blocks >= n_sink + n_window, and n_prev == 0 or
+ * n_prev >= n_sink + n_window.
  */
-int oracle_select(int64_t R, int n_blocks, int kq, int ke, int n_prev,
-                  const double *s, const float *e, int64_t e_stride,
-                  int32_t *agn_state, int32_t *selected, uint8_t *is_agn)
+int oracle_select_sw(int64_t R, int n_blocks, int kq, int ke, int n_sink, int n_window, int n_prev,
+                     const double *s, const float *e, int64_t e_stride,
+                     int32_t *agn_state, int32_t *selected, uint8_t *is_agn)
 {
     const int k = kq + ke;
     if (R < 0 || n_blocks <= 0 || kq < 0 || ke < 0 || k <= 0 || k > n_blocks || n_prev < 0 ||
-        n_prev > n_blocks || e_stride < n_blocks)
+        n_prev > n_blocks || e_stride < n_blocks || n_sink < 0 || n_window < 0 ||
+        n_sink + n_window > ke || n_blocks < n_sink + n_window ||
+        (n_prev > 0 && n_prev < n_sink + n_window))
         return -1;
+    const int n_dyn = ke - n_sink - n_window;
     int status = 0;
 #pragma omp parallel for schedule(dynamic) reduction(min : status)
     for (int64_t r = 0; r < R; r++) {
+        uint8_t *prevE = calloc((size_t)n_blocks, 1);
         uint8_t *candE = calloc((size_t)n_blocks, 1);
         uint8_t *inE = calloc((size_t)n_blocks, 1);
         uint8_t *candQ = calloc((size_t)n_blocks, 1);
         uint8_t *inQ = calloc((size_t)n_blocks, 1);
         double *ekey = malloc(sizeof(double) * (size_t)n_blocks);
-        int bad = (!candE || !inE || !candQ || !inQ || !ekey);
+        int bad = (!prevE || !candE || !inE || !candQ || !inQ || !ekey);
         if (!bad) {
             for (int i = 0; i < n_blocks; i++)
                 ekey[i] = (double)e[(size_t)r * e_stride + i];
-            if (n_prev == 0) {
-                for (int i = 0; i < n_blocks; i++)
-                    candE[i] = 1;
-            } else {
+            if (n_prev > 0) {
                 for (int j = 0; j < ke; j++) {
                     int id = agn_state[(size_t)r * ke + j];
                     if (id < 0 || id >= n_prev)
                         bad = 1;
                     else
-                        candE[id] = 1;
+                        prevE[id] = 1;
                 }
-                for (int i = n_prev; i < n_blocks; i++)
+            }
+            for (int i = 0; i < n_blocks; i++) {
+                const int fixed = (i < n_sink) || (i >= n_blocks - n_window);
+                if (fixed) {
+                    inE[i] = 1;
+                    continue;
+                }
+                if (n_prev == 0)
                     candE[i] = 1;
+                else if (i < n_prev - n_window)
+                    candE[i] = prevE[i];
+                else
+                    candE[i] = 1;   /* left the window, or visible past it, since the last step */
             }
         }
-        if (!bad && topk_plain(n_blocks, ekey, candE, ke, inE) != 0)
+        if (!bad && topk_plain(n_blocks, ekey, candE, n_dyn, inE) != 0)
             bad = 1;
         if (!bad) {
             for (int i = 0; i < n_blocks; i++)
@@ -238,6 +257,7 @@ int oracle_select(int64_t R, int n_blocks, int kq, int ke, int n_prev,
                 }
             }
         }
+        free(prevE);
         free(candE);
         free(inE);
         free(candQ);
@@ -247,6 +267,14 @@ int oracle_select(int64_t R, int n_blocks, int kq, int ke, int n_prev,
             status = -2;
     }
     return status;
+}
+
+/* The selection without sink and window blocks: every query-agnostic member is score-ranked. */
+int oracle_select(int64_t R, int n_blocks, int kq, int ke, int n_prev,
+                  const double *s, const float *e, int64_t e_stride,
+                  int32_t *agn_state, int32_t *selected, uint8_t *is_agn)
+{
+    return oracle_select_sw(R, n_blocks, kq, ke, 0, 0, n_prev, s, e, e_stride, agn_state, selected, is_agn);
 }
 
 /*

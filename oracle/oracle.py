@@ -47,6 +47,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_pool_keys.argtypes = [I64, I64, I, I, P, I, P]
         L.oracle_block_scores.argtypes = [I, I, I, I, I, I, P, I, P, I64, P]
         L.oracle_select.argtypes = [I64, I, I, I, I, P, P, I64, P, P, P]
+        L.oracle_select_sw.argtypes = [I64, I, I, I, I, I, I, P, P, I64, P, P, P]
         L.oracle_cache_step.argtypes = [I64, I, I, I, P, P, P, P, P, P]
         L.oracle_gather.argtypes = [I64, I, I, I, I64, P, P, P, P]
         L.oracle_attention.argtypes = [I, I, I, I, I, I, I, P, I, P, P, I, P, D, P]
@@ -111,11 +112,13 @@ def block_scores(q: np.ndarray, kp: np.ndarray, n_blocks: int, spb: int) -> np.n
 
 
 def select(s: np.ndarray, evict: np.ndarray, kq: int, ke: int, n_prev: int = 0,
-           agn_state: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+           agn_state: Optional[np.ndarray] = None, n_sink: int = 0,
+           n_window: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """s: [B, Hkv, n_blocks] float64; evict: [B, Hkv, >=n_blocks] float32.
 
-    Returns (selected [B,Hkv,k] int32 ascending, agn_state [B,Hkv,ke] int32 ascending,
-    is_agn [B,Hkv,k] bool)."""
+    n_sink / n_window: blocks at the start / end of the visible context that always belong to
+    the query-agnostic subset.  Returns (selected [B,Hkv,k] int32 ascending, agn_state
+    [B,Hkv,ke] int32 ascending, is_agn [B,Hkv,k] bool)."""
     B, Hkv, n = s.shape
     k = kq + ke
     s = np.ascontiguousarray(s, dtype=np.float64)
@@ -124,8 +127,8 @@ def select(s: np.ndarray, evict: np.ndarray, kq: int, ke: int, n_prev: int = 0,
         np.ascontiguousarray(agn_state, dtype=np.int32).copy()
     sel = np.empty((B, Hkv, k), dtype=np.int32)
     isa = np.empty((B, Hkv, k), dtype=np.uint8)
-    _check(lib().oracle_select(B * Hkv, n, kq, ke, n_prev, _ptr(s), _ptr(ev), ev.shape[-1],
-                               _ptr(st) if ke > 0 else None, _ptr(sel), _ptr(isa)), "select")
+    _check(lib().oracle_select_sw(B * Hkv, n, kq, ke, n_sink, n_window, n_prev, _ptr(s), _ptr(ev), ev.shape[-1],
+                                  _ptr(st) if ke > 0 else None, _ptr(sel), _ptr(isa)), "select")
     return sel, st, isa.astype(bool)
 
 
@@ -216,9 +219,9 @@ def locality(prev: np.ndarray, cur: np.ndarray, nbmax: int) -> np.ndarray:
 
 def decode_step(q: np.ndarray, kp: np.ndarray, evict: np.ndarray, k_store: np.ndarray, v_store: np.ndarray,
                 n_blocks: int, kq: int, ke: int, spb: int, n_prev: int = 0,
-                agn_state: Optional[np.ndarray] = None) -> dict:
+                agn_state: Optional[np.ndarray] = None, n_sink: int = 0, n_window: int = 0) -> dict:
     """One GPU-resident decode step in the pages' order: scores, selection, attention."""
     s = block_scores(q, kp, n_blocks, spb)
-    sel, st, isa = select(s, evict, kq, ke, n_prev, agn_state)
+    sel, st, isa = select(s, evict, kq, ke, n_prev, agn_state, n_sink, n_window)
     out = attention(q, k_store, v_store, sel)
     return {"scores": s, "selected": sel, "agn_state": st, "is_agn": isa, "out": out}

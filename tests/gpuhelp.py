@@ -50,7 +50,7 @@ def shape_of(w: Workload, *, sub_block_size=32, n_blocks=None, decode_splits=0, 
                         n_blocks=w.n_blocks if n_blocks is None else n_blocks, n_blocks_max=w.nbmax,
                         kq=w.kq, ke=w.ke, sub_block_size=sub_block_size, cache_slots=w.cache_slots,
                         dtype=N.NOSA_BF16 if w.dtype == "bf16" else N.NOSA_F32, decode_splits=decode_splits,
-                        select_parts=select_parts)
+                        select_parts=select_parts, sink_blocks=w.n_sink, window_blocks=w.n_window)
 
 
 def gpu_pool(shape: N.NosaShape, k_dev: torch.Tensor) -> torch.Tensor:
@@ -95,7 +95,7 @@ def check_attention(out_gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str 
 
 
 def check_selection(sel_gpu: np.ndarray, agn_gpu: np.ndarray, s_oracle: np.ndarray, evict: np.ndarray,
-                    kq: int, ke: int, n_prev: int = 0, agn_prev=None) -> int:
+                    kq: int, ke: int, n_prev: int = 0, agn_prev=None, n_sink: int = 0, n_window: int = 0) -> int:
     """Compare a GPU selection with the oracle's on the same inputs.
 
     Gamma_e compares raw eviction scores, so it must match exactly.  The full selection must match
@@ -103,7 +103,7 @@ def check_selection(sel_gpu: np.ndarray, agn_gpu: np.ndarray, s_oracle: np.ndarr
     within TIE_REL of each other; then any set is accepted that holds every block scored clearly
     above the kq-th score, no block clearly below it, and exactly kq blocks.
     Returns the number of rows decided inside the tie band."""
-    sel_o, agn_o, _ = O.select(s_oracle, evict, kq, ke, n_prev, agn_prev)
+    sel_o, agn_o, _ = O.select(s_oracle, evict, kq, ke, n_prev, agn_prev, n_sink, n_window)
     B, H, n = s_oracle.shape
     k = kq + ke
     sel_gpu = sel_gpu.reshape(B, H, k)

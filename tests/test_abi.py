@@ -62,6 +62,9 @@ BAD = [
     (dict(n_blocks_max=20000, n_blocks=256), N.NOSA_EUNSUPPORTED),
     (dict(batch=0), N.NOSA_EINVAL),
     (dict(decode_splits=-2), N.NOSA_EINVAL),
+    (dict(sink_blocks=-1), N.NOSA_EINVAL),
+    (dict(sink_blocks=1, window_blocks=32), N.NOSA_EINVAL),   # sink + window > ke
+    (dict(kq=1, ke=8, window_blocks=8, n_blocks=9, n_blocks_max=9, sink_blocks=1), N.NOSA_EINVAL),
 ]
 
 
@@ -86,6 +89,7 @@ def test_invalid_pointers_rejected_on_host():
         lambda: N.nosa_select(s, 16, 16, 16, 0, 16, 16, 128, stream=0),         # ws misaligned
         lambda: N.nosa_select(s, 16, 16, 16, 300, 16, 16, 256, stream=0),       # n_blocks_prev > n_blocks
         lambda: N.nosa_select(s, 16, 16, 16, -1, 16, 16, 256, stream=0),
+        lambda: N.nosa_select(s.copy(sink_blocks=1, window_blocks=16), 16, 16, 16, 10, 16, 16, 256, stream=0),
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 0, 16, 0.1, 16, 256, stream=0),    # store_blocks 0
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, -1.0, 16, 256, stream=0), # bad scale
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, float("nan"), 16, 256, stream=0),

@@ -15,7 +15,7 @@ from oracle import oracle as O  # noqa: E402
 from tests import gpuhelp as H  # noqa: E402
 
 
-@pytest.mark.parametrize("cfg", ["C2", "C3", "C5"])
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C5", "F1"])
 def test_resident_config_end_to_end(cfg):
     w = WORKLOADS[cfg]
     x = generate(w)
@@ -29,7 +29,8 @@ def test_resident_config_end_to_end(cfg):
     kp_ref = O.pool_keys(x["k"], 32)
     np.testing.assert_allclose(H.host(kp).reshape(kp_ref.shape), kp_ref, rtol=1e-6, atol=1e-6)
     s_ref = O.block_scores(x["q"], kp_ref, w.n_blocks, 2)
-    ties = H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke)
+    ties = H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke, n_sink=w.n_sink,
+                             n_window=w.n_window)
     sel_h = H.host(sel).reshape(w.batch, w.n_kv_heads, w.k)
     ref = O.attention(x["q"], x["k"], x["v"], sel_h)
     stats = H.check_attention(H.host(out), ref, w.dtype, cfg)

@@ -312,3 +312,33 @@ def test_select_many_rows_one_workgroup_each():
     out = H.gpu_decode(shape, q_dev, H.dev(x["k"]), H.dev(x["v"]), w.nbmax, sel, ws)
     ref = O.attention(x["q"], x["k"], x["v"], H.host(sel).reshape(w.batch, w.n_kv_heads, w.k))
     H.check_attention(H.host(out), ref, "bf16", "wide")
+
+
+@pytest.mark.parametrize("n,kq,ke,ns,nw,parts", [(40, 4, 10, 1, 4, 0), (64, 6, 12, 1, 11, 3), (300, 16, 48, 1, 16, 0),
+                                                 (700, 16, 48, 2, 16, 0), (33, 3, 9, 0, 9, 1), (50, 5, 3, 3, 0, 0)])
+def test_select_sink_window(n, kq, ke, ns, nw, parts):
+    # Sink and window blocks always join the query-agnostic subset; the rest is ranked by
+    # eviction score under strict eviction, over a few steps with blocks arriving.
+    rng = np.random.default_rng(n + nw)
+    B, Hkv, G, d = 2, 2, 4, 128
+    nbmax = n + 12
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    kp = rng.standard_normal((B, Hkv, nbmax * 2, d)).astype(np.float32)
+    ev = rng.random((B, Hkv, nbmax), dtype=np.float32)
+    shape0 = N.make_shape(batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=d, n_blocks=n, n_blocks_max=nbmax,
+                          kq=kq, ke=ke, dtype=N.NOSA_F32, select_parts=parts, sink_blocks=ns, window_blocks=nw)
+    ws = N.workspace(shape0)
+    q_dev, kp_dev, ev_dev = H.dev(q), H.dev(kp), H.dev(ev)
+    kp64 = kp.astype(np.float64)
+    agn_dev, agn_ref, cur, prev = None, None, n, 0
+    for step, grow in enumerate([0, 1, 0, 3, 2, 1]):
+        cur = min(nbmax, cur + grow)
+        shape = shape0.copy(n_blocks=cur)
+        sel, agn_dev = H.gpu_select(shape, q_dev, kp_dev, ev_dev, ws, n_prev=prev, agn=agn_dev)
+        s_ref = O.block_scores(q, kp64[:, :, :2 * cur], cur, 2)
+        H.check_selection(H.host(sel), H.host(agn_dev), s_ref, ev, kq, ke, prev, agn_ref, ns, nw)
+        _, agn_ref, _ = O.select(s_ref, ev, kq, ke, prev, agn_ref, ns, nw)
+        E = H.host(agn_dev)
+        for r in range(B * Hkv):
+            assert set(range(ns)) | set(range(cur - nw, cur)) <= set(E[r].tolist())
+        prev = cur

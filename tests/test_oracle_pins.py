@@ -393,3 +393,60 @@ def test_c1_regression_record():
     assert r["agn_state"].reshape(-1).tolist() == rec["agn_state"]
     np.testing.assert_allclose(r["scores"].reshape(-1), rec["block_scores"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(r["out"].reshape(-1), rec["out"], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# Sink and sliding-window blocks inside the query-agnostic budget ([P1] B.2.2: the paper's
+# query-agnostic blocks include one attention-sink block and a window of recent blocks)
+# --------------------------------------------------------------------------------------
+
+def test_sink_window_hand_worked_example():
+    # ke = 4 = 1 sink + 2 window + 1 score-ranked block; kq = 1.
+    e = np.array([[[0.9, 0.1, 0.5, 0.7, 0.2, 0.3, 0.8, 0.05, 0.6, 0.95]]], np.float32)
+    kw = dict(kq=1, ke=4, n_sink=1, n_window=2)
+    # step 0, 8 blocks: fixed {0} + window {6, 7}; ranked candidates {1..5} -> 3 (e 0.7)
+    sel, st, _ = O.select(np.arange(1.0, 9.0).reshape(1, 1, 8), e, **kw)
+    assert st.tolist() == [[[0, 3, 6, 7]]]
+    assert sel.tolist() == [[[0, 3, 5, 6, 7]]]        # query-aware: best of {1,2,4,5} = 5
+    # step 1, block 8 arrives: window {7, 8}; block 6 left the window and competes with the
+    # ranked member 3: e 0.8 > 0.7 -> 6 stays, 3 leaves Gamma_e for good (but may be recalled)
+    s1 = np.zeros((1, 1, 9))
+    s1[0, 0, 3] = 100.0
+    sel, st, _ = O.select(s1, e, n_prev=8, agn_state=st, **kw)
+    assert st.tolist() == [[[0, 6, 7, 8]]]
+    assert sel.tolist() == [[[0, 3, 6, 7, 8]]]
+    # step 2, block 9 arrives: block 7 (e 0.05) leaves the window and loses to 6
+    sel, st, _ = O.select(np.zeros((1, 1, 10)), e, n_prev=9, agn_state=st, **kw)
+    assert st.tolist() == [[[0, 6, 8, 9]]]
+    # no score-ranked slot: Gamma_e is exactly sink + window
+    sel, st, _ = O.select(np.zeros((1, 1, 10)), e, kq=2, ke=3, n_sink=1, n_window=2)
+    assert st.tolist() == [[[0, 8, 9]]]
+
+
+def test_sink_window_multistep_invariants():
+    rng = np.random.default_rng(13)
+    B, H, kq, ke, ns, nw, n0, nmax, steps = 2, 2, 5, 12, 1, 4, 30, 60, 40
+    e = rng.random((B, H, nmax), dtype=np.float32)
+    n, st, prev_sel, prev_st = n0, None, None, None
+    left_for_good = [[set() for _ in range(H)] for _ in range(B)]
+    for t in range(steps):
+        n_prev = 0 if t == 0 else n
+        if t > 0 and rng.random() < 0.6 and n < nmax:
+            n += int(rng.integers(1, 3))
+            n = min(n, nmax)
+        s = rng.standard_normal((B, H, n))
+        sel, st, _ = O.select(s, e, kq, ke, n_prev=n_prev, agn_state=st, n_sink=ns, n_window=nw)
+        for b in range(B):
+            for h in range(H):
+                E = set(st[b, h].tolist())
+                assert set(range(ns)) <= E and set(range(n - nw, n)) <= E
+                assert len(E) == ke and len(set(sel[b, h].tolist())) == kq + ke
+                assert not (E & left_for_good[b][h])
+                if prev_st is not None:
+                    E0 = set(prev_st[b, h].tolist())
+                    left_for_good[b][h] |= E0 - E
+                    arrivals = n - n_prev
+                    assert len(E0 & E) >= ke - arrivals
+                    overlap = len(set(prev_sel[b, h].tolist()) & set(sel[b, h].tolist()))
+                    assert overlap >= ke - arrivals
+        prev_sel, prev_st = sel, st.copy()
