@@ -26,8 +26,9 @@
 //   are compacted in ascending block id.
 // Launch plans (chosen on the host).  "fused": one workgroup (256 or 1024 threads) scores a
 //   whole row and selects from LDS.  "parts": several 256-thread workgroups score slices of a
-//   row into the workspace and a second kernel (1024 threads per row) selects.  No workgroup
-//   ever waits on another inside a kernel.
+//   row into the workspace while one more workgroup per row picks Gamma_e from the eviction
+//   scores; a second kernel (1024 threads per row) picks Gamma_q.  No workgroup ever waits on
+//   another inside a kernel.
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
@@ -238,7 +239,7 @@ __device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, i
     int ps = (incl - cnt) & 0xFFFF, pe = (incl - cnt) >> 16;
     for (int i = lo; i < hi; ++i) {
         if (inE[i]) {
-            if (pe < ke) agn[pe] = i;
+            if (agn && pe < ke) agn[pe] = i;
             ++pe;
         }
         if (inE[i] | inQ[i]) {
@@ -250,7 +251,8 @@ __device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, i
     __syncthreads();
     const int ns = sh.bcast[2] & 0xFFFF, ne = sh.bcast[2] >> 16;
     for (int p = ns + tid; p < k; p += NT) sel[p] = -1;
-    for (int p = ne + tid; p < ke; p += NT) agn[p] = -1;
+    if (agn)
+        for (int p = ne + tid; p < ke; p += NT) agn[p] = -1;
 }
 
 // LDS layout of the selection phase for a row of n blocks.
@@ -312,9 +314,11 @@ __device__ __forceinline__ void ev_store(const RowLds &L, int n, const float (&e
     }
 }
 
-// Selection of one row from the block scores in L.sc (all threads of the workgroup).
+// Gamma_e of one row into L.inE (all threads of the workgroup): the sink and window blocks plus
+// the score-ranked members under strict eviction.  Reads the previous Gamma_e from agn_state; uses
+// L.inQ as scratch and leaves it cleared.
 template <int NT>
-__device__ void select_row(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh) {
+__device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh) {
     const int tid = threadIdx.x;
     const int n = a.n_blocks;
     for (int i = tid; i < n; i += NT) {
@@ -322,8 +326,6 @@ __device__ void select_row(const SelectArgs &a, int row, const RowLds &L, Select
         L.inQ[i] = 0;
     }
     __syncthreads();
-
-    // Gamma_e: sink and window blocks, plus the score-ranked members under strict eviction
     const int n_prev = a.n_prev;
     const bool fresh = (n_prev == 0);
     const int w_lo = n - a.n_window;              // first window block
@@ -345,16 +347,19 @@ __device__ void select_row(const SelectArgs &a, int row, const RowLds &L, Select
         [&](int i) { return i >= n_sink && i < w_lo && (fresh || i >= left || prevE[i]); }, L.inE, L.keys, sh);
     for (int i = tid; i < n; i += NT) L.inQ[i] = 0;
     __syncthreads();
+}
 
-    // Gamma_q: query-aware subset over the complement of Gamma_e
+// Gamma_q of one row from the block scores in L.sc and Gamma_e in L.inE, then the outputs in
+// ascending block id: the selection, and agn_state when write_agn is set.
+template <int NT>
+__device__ void select_query(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh, bool write_agn) {
+    const int n = a.n_blocks;
     const uint8_t *inE = L.inE;
     const float *sc = L.sc;
     topk_mark<NT>(
         n, a.kq, [&](int i) { return order_key(sc[i]); }, [&](int i) { return !inE[i]; }, L.inQ, L.keys, sh);
-
-    // outputs, ascending block id
     const int k = a.kq + a.ke;
-    compact_outputs<NT>(n, L.inE, L.inQ, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
+    compact_outputs<NT>(n, L.inE, L.inQ, (write_agn && a.ke > 0) ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
                         a.sel + (size_t)row * k, k, sh);
 }
 
@@ -450,32 +455,54 @@ __global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
     score_range<T, D, SPB, NT>(a, row, 0, a.n_blocks, L.sc, nullptr);
     ev_store<NT>(L, a.n_blocks, e);
     __syncthreads();
-    select_row<NT>(a, row, L, sh);
+    select_agnostic<NT>(a, row, L, sh);
+    select_query<NT>(a, row, L, sh, true);
 }
 
-// A slice of a row's blocks, scored into the global score buffer.
+// Grid rows x (parts + 1): workgroup `part < parts` scores a slice of the row's blocks into the
+// global score buffer; the extra workgroup `part == parts` (absent in scores-only mode) computes
+// the row's Gamma_e from the eviction scores meanwhile and writes it to agn_state.
 template <typename T, int D, int SPB>
 __global__ __launch_bounds__(256) void score_part_kernel(SelectArgs a) {
-    const int row = blockIdx.x / a.parts, part = blockIdx.x - row * a.parts;
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ SelectShared<256> sh;
+    const int nparts = a.parts + (a.scores_only ? 0 : 1);
+    const int row = blockIdx.x / nparts, part = blockIdx.x - row * nparts;
+    if (part == a.parts) {
+        const RowLds L = carve<256>(dyn, a.n_blocks);
+        float e[kEvPre];
+        ev_load<256>(a, row, e);
+        ev_store<256>(L, a.n_blocks, e);
+        select_agnostic<256>(a, row, L, sh);
+        compact_outputs<256>(a.n_blocks, L.inE, L.inE, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
+                             nullptr, 0, sh);
+        return;
+    }
     const int blk_lo = part * a.blocks_per_part;
     const int blk_hi = min(a.n_blocks, blk_lo + a.blocks_per_part);
     score_range<T, D, SPB, 256>(a, row, blk_lo, blk_hi, nullptr, a.scores + (size_t)row * a.scores_stride);
 }
 
-// Selection of rows scored by score_part_kernel: one workgroup per row.
+// Gamma_q of rows scored by score_part_kernel (Gamma_e is already in agn_state): one workgroup per row.
 template <int NT>
 __global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ SelectShared<NT> sh;
     const int row = blockIdx.x;
     const RowLds L = carve<NT>(dyn, a.n_blocks);
-    float e[kEvPre];
-    ev_load<NT>(a, row, e);
     const float *gscore = a.scores + (size_t)row * a.scores_stride;
-    for (int i = threadIdx.x; i < a.n_blocks; i += NT) L.sc[i] = gscore[i];
-    ev_store<NT>(L, a.n_blocks, e);
+    for (int i = threadIdx.x; i < a.n_blocks; i += NT) {
+        L.sc[i] = gscore[i];
+        L.inE[i] = 0;
+        L.inQ[i] = 0;
+    }
     __syncthreads();
-    select_row<NT>(a, row, L, sh);
+    for (int j = threadIdx.x; j < a.ke; j += NT) {
+        const int id = a.agn[(size_t)row * a.ke + j];
+        if (id >= 0 && id < a.n_blocks) L.inE[id] = 1;
+    }
+    __syncthreads();
+    select_query<NT>(a, row, L, sh, false);
 }
 
 size_t select_lds_bytes(int n_blocks) { return row_lds_bytes<1024>(n_blocks); }
@@ -503,7 +530,10 @@ static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threa
         }
         return hipGetLastError();
     }
-    score_part_kernel<T, D, SPB><<<dim3((unsigned)(rows * a.parts)), dim3(256), 0, st>>>(a);
+    const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<256>(a.n_blocks);
+    if ((e = allow_lds(score_part_kernel<T, D, SPB>, dyn0)) != hipSuccess) return e;
+    score_part_kernel<T, D, SPB>
+        <<<dim3((unsigned)(rows * (a.parts + (a.scores_only ? 0 : 1)))), dim3(256), dyn0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess || a.scores_only) return e;
     const size_t dyn = row_lds_bytes<1024>(a.n_blocks);
     if ((e = allow_lds(pick_kernel<1024>, dyn)) != hipSuccess) return e;
