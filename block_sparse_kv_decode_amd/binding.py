@@ -12,6 +12,12 @@ import ctypes
 import os
 from typing import Any, Optional
 
+# torch is imported before the library is opened, so that libnosa.so binds to the HIP runtime
+# torch has already loaded.  Opened first, it would load the system HIP runtime, and torch would
+# then load its own bundled copy: two runtimes in one process, each blind to the other's
+# allocations and streams.
+import torch  # noqa: F401,E402
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # NOSA_LIBRARY selects another build of the same library (e.g. an experimental variant).
 LIB_PATH = os.environ.get("NOSA_LIBRARY") or os.path.join(_PKG, "libnosa.so")
@@ -20,8 +26,8 @@ NOSA_OK, NOSA_EINVAL, NOSA_EUNSUPPORTED, NOSA_ECAPACITY, NOSA_EHIP = 0, -1, -2, 
 NOSA_F32, NOSA_BF16 = 0, 1
 
 EXPORTED = (
-    "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_block_scores",
-    "nosa_select", "nosa_cache_update", "nosa_sparse_decode",
+    "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
+    "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode",
 )
 
 
@@ -64,7 +70,7 @@ def make_shape(*, batch, n_q_heads, n_kv_heads, head_dim, n_blocks, kq, ke, n_bl
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libnosa.so is not built (%s); run `python -m block_sparse_kv_decode_amd.build` "
+        raise ImportError("libnosa.so is not built (%s); run `python block_sparse_kv_decode_amd/build.py` "
                           "or __graft_entry__.build()" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     P, I32, SP = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(NosaShape)
@@ -76,6 +82,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_workspace_bytes.argtypes = [SP]
     L.nosa_pool_keys.restype = ctypes.c_int
     L.nosa_pool_keys.argtypes = [SP, P, I32, I32, P, P]
+    L.nosa_append_kv.restype = ctypes.c_int
+    L.nosa_append_kv.argtypes = [SP, P, P, P, P, P, P, P, P]
     L.nosa_block_scores.restype = ctypes.c_int
     L.nosa_block_scores.argtypes = [SP, P, P, P, P, P]
     L.nosa_select.restype = ctypes.c_int
@@ -132,6 +140,11 @@ def nosa_workspace_bytes(shape: NosaShape) -> int:
 def nosa_pool_keys(shape, k, first_block, n_new, pooled_k, stream=None) -> None:
     _check(lib.nosa_pool_keys(ctypes.byref(shape), _p(k), int(first_block), int(n_new), _p(pooled_k),
                               _stream(stream)))
+
+
+def nosa_append_kv(shape, k_new, v_new, positions, k_store, v_store, pool_acc, pooled_k, stream=None) -> None:
+    _check(lib.nosa_append_kv(ctypes.byref(shape), _p(k_new), _p(v_new), _p(positions), _p(k_store), _p(v_store),
+                              _p(pool_acc), _p(pooled_k), _stream(stream)))
 
 
 def nosa_block_scores(shape, q, pooled_k, scores, ws, stream=None) -> None:

@@ -1,7 +1,8 @@
 """Build the gfx950 HIP library ``libnosa.so`` in-tree with hipcc.
 
-``python -m block_sparse_kv_decode_amd.build`` compiles every source under ``csrc/`` for
-gfx950 and links ``block_sparse_kv_decode_amd/libnosa.so``.  No GPU is needed to build.
+``python block_sparse_kv_decode_amd/build.py`` (or ``__graft_entry__.build()``) compiles every
+source under ``csrc/`` for gfx950 and links ``block_sparse_kv_decode_amd/libnosa.so``.  No GPU is
+needed to build.  It is run by path, not as ``-m``: importing the package loads the library.
 """
 
 from __future__ import annotations

@@ -188,6 +188,32 @@ int get_events(DeviceEvents **out) {
     return NOSA_OK;
 }
 
+// Device address of a caller buffer: device memory as is, pinned host memory through its device
+// mapping.  Pageable host memory is rejected.
+int device_address(const void *p, void **out, const char *what) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NOSA_EINVAL, "%s is neither device memory nor pinned host memory (%s)", what, hipGetErrorString(e));
+    }
+    if (attr.type == hipMemoryTypeHost) {
+        void *d = nullptr;
+        e = hipHostGetDevicePointer(&d, const_cast<void *>(p), 0);
+        if (e != hipSuccess || !d) {
+            (void)hipGetLastError();
+            return fail(NOSA_EINVAL, "%s: pinned host memory without a device mapping (%s)", what, hipGetErrorString(e));
+        }
+        *out = d;
+        return NOSA_OK;
+    }
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged || attr.type == hipMemoryTypeUnified) {
+        *out = const_cast<void *>(p);
+        return NOSA_OK;
+    }
+    return fail(NOSA_EINVAL, "%s is neither device memory nor pinned host memory", what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,6 +248,36 @@ int nosa_pool_keys(const nosa_shape *shape, const void *k, int32_t first_block, 
     a.sbs = shape->sub_block_size;
     hipError_t e = launch_pool(shape->dtype, shape->head_dim, a, rows_of(shape), stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pool_keys launch");
+}
+
+int nosa_append_kv(const nosa_shape *shape, const void *k_new, const void *v_new, const int32_t *positions,
+                   void *k_store, void *v_store, float *pool_acc, float *pooled_k, hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    REQUIRE_PTR(k_new, 16);
+    REQUIRE_PTR(v_new, 16);
+    REQUIRE_PTR(positions, 4);
+    REQUIRE_PTR(k_store, 16);
+    REQUIRE_PTR(v_store, 16);
+    REQUIRE_PTR(pool_acc, 16);
+    REQUIRE_PTR(pooled_k, 16);
+    void *dk = nullptr, *dv = nullptr;
+    if ((rc = device_address(k_store, &dk, "k_store")) != NOSA_OK) return rc;
+    if ((rc = device_address(v_store, &dv, "v_store")) != NOSA_OK) return rc;
+    AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.positions = positions;
+    a.k_store = dk;
+    a.v_store = dv;
+    a.acc = pool_acc;
+    a.kp = pooled_k;
+    a.Hkv = shape->n_kv_heads;
+    a.n_blocks_max = shape->n_blocks_max;
+    a.spb = spb_of(shape);
+    a.sbs = shape->sub_block_size;
+    hipError_t e = launch_append(shape->dtype, shape->head_dim, a, rows_of(shape), stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "append_kv launch");
 }
 
 static int run_scores(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,

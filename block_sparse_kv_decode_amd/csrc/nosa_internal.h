@@ -21,6 +21,15 @@ struct PoolArgs {
     int sbs;              // tokens per sub-block
 };
 
+struct AppendArgs {
+    const void *k_new, *v_new;   // [R, d] the new token's key / value
+    const int32_t *positions;    // [B] index of the new token in each sequence
+    void *k_store, *v_store;     // [R, nbmax, 64, d], device addresses
+    float *acc;                  // [R, d] running sum of the open sub-block
+    float *kp;                   // [R, nbmax * spb, d]
+    int Hkv, n_blocks_max, spb, sbs;
+};
+
 struct SelectArgs {
     const void *q;        // [B, Hq, d]
     const float *kp;      // [R, nbmax * spb, d]
@@ -70,6 +79,7 @@ struct DecodeArgs {
 
 // Each launcher returns hipSuccess or the error of the launch.
 hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_t st);
+hipError_t launch_append(int dtype, int d, const AppendArgs &a, int rows, hipStream_t st);
 // fused_threads: workgroup size (256 or 1024) of the one-workgroup-per-row plan (parts == 1).
 hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads, hipStream_t st);
 size_t select_lds_bytes(int n_blocks);

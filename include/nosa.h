@@ -13,7 +13,8 @@
  *   3. (offloaded KV only) hit/miss check against the GPU block cache, replacement map and
  *      host-to-GPU copy of the missed blocks                  -> nosa_cache_update ([P1] §4, App. A)
  *   4. GQA attention over the tokens of the selected blocks  -> nosa_sparse_decode ([P1] App. A)
- * Pooled keys (sub-block means) are state kept next to the KV cache -> nosa_pool_keys ([P1] §3.1).
+ * Pooled keys (sub-block means) are state kept next to the KV cache -> nosa_pool_keys ([P1] §3.1),
+ * extended token by token by the decode append path -> nosa_append_kv.
  *
  * Conventions for every entry point
  *   - All buffers are owned by the caller.  Device pointers point to GPU memory of the current
@@ -100,6 +101,28 @@ size_t nosa_workspace_bytes(const nosa_shape *shape);
  */
 int nosa_pool_keys(const nosa_shape *shape, const void *k, int32_t first_block, int32_t n_new,
                    float *pooled_k, hipStream_t stream);
+
+/*
+ * Decode append path: one new token per sequence joins the KV stores and the pooled keys
+ * ([P1] §3.1: pooled sub-block keys; [P4] Method 1: strict eviction applies to blocks as they
+ * arrive).  For every row r = (b, g), with p = positions[b] (the token's index in sequence b):
+ *   k_store[r][p / block_size][p % block_size] = k_new[r], and the same for v;
+ *   pool_acc[r] = (p % sub_block_size == 0 ? 0 : pool_acc[r]) + k_new[r]   (float32);
+ *   when (p + 1) % sub_block_size == 0: pooled_k[r][p / sub_block_size] = pool_acc[r] / sub_block_size.
+ * The sums run in token order from 0, as in nosa_pool_keys, so both give bit-identical pooled keys.
+ * A block whose last token is appended becomes visible to nosa_select at the next step (pass the
+ * previous n_blocks as n_blocks_prev, so it competes for the query-agnostic subset as an arrival).
+ *   k_new, v_new : device, [B, Hkv, d], dtype
+ *   positions    : device, [B] int32; rows whose position lies outside [0, n_blocks_max * block_size)
+ *                  are skipped
+ *   k_store, v_store : [B, Hkv, n_blocks_max, block_size, d], dtype; device memory, or pinned host
+ *                  memory (written through its device mapping: the offloaded host pool)
+ *   pool_acc     : device, [B, Hkv, d] float32, running sums of the open sub-blocks (state kept by
+ *                  the caller between calls; no initial contents needed)
+ *   pooled_k     : device, as in nosa_pool_keys
+ */
+int nosa_append_kv(const nosa_shape *shape, const void *k_new, const void *v_new, const int32_t *positions,
+                   void *k_store, void *v_store, float *pool_acc, float *pooled_k, hipStream_t stream);
 
 /*
  * Query-aware block scores only (the scoring half of nosa_select, exposed for inspection;

@@ -205,6 +205,24 @@ def attention_masked(q: np.ndarray, k_store: np.ndarray, v_store: np.ndarray, ma
     return out
 
 
+def append_kv(k_store: np.ndarray, v_store: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+              positions: np.ndarray) -> None:
+    """Decode append, in place ([P1] paperlayer.ai summary §3.1, pooled keys kept beside the cache;
+    [P4] gist.science technical summary, Method 1, blocks arriving under strict eviction).
+
+    stores: [B, Hkv, nbmax, bs, d]; k_new, v_new: [B, Hkv, d]; positions: [B] token index of the
+    new token, or outside [0, nbmax * bs) to leave sequence b unchanged.  Token p of a sequence is
+    token p % bs of block p // bs.  The pooled key of a sub-block is then ``pool_keys`` of the
+    store once its last token has been written."""
+    B, Hkv, nbmax, bs, d = k_store.shape
+    for b in range(B):
+        p = int(positions[b])
+        if p < 0 or p >= nbmax * bs:
+            continue
+        k_store[b, :, p // bs, p % bs, :] = k_new[b]
+        v_store[b, :, p // bs, p % bs, :] = v_new[b]
+
+
 def locality(prev: np.ndarray, cur: np.ndarray, nbmax: int) -> np.ndarray:
     """gamma per row = |prev ∩ cur| / k."""
     k = cur.shape[-1]

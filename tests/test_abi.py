@@ -118,3 +118,26 @@ def test_cache_update_rejects_small_cache_and_null():
 
 def test_pool_keys_zero_blocks_is_a_noop():
     N.nosa_pool_keys(_good(), 16, 5, 0, 16, stream=0)   # validates, launches nothing
+
+
+def test_append_rejects_bad_pointers_on_host():
+    s = _good()
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_append_kv(s, 16, 16, None, 16, 16, 16, 16, stream=0)
+    assert ei.value.code == N.NOSA_EINVAL
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_append_kv(s, 16, 8, 16, 16, 16, 16, 16, stream=0)      # v_new misaligned
+    assert ei.value.code == N.NOSA_EINVAL
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_append_kv(_good(head_dim=96), 16, 16, 16, 16, 16, 16, 16, stream=0)
+    assert ei.value.code == N.NOSA_EUNSUPPORTED
+
+
+def test_one_hip_runtime_in_the_process():
+    # The library shares torch's HIP runtime: importing the package (which imports torch first)
+    # maps exactly one libamdhip64 into the process.
+    code = ("import block_sparse_kv_decode_amd, torch\n"
+            "m = sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l})\n"
+            "print(len(m)); print(m)\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True, cwd=ROOT).stdout
+    assert out.splitlines()[0] == "1", out

@@ -450,3 +450,40 @@ def test_sink_window_multistep_invariants():
                     overlap = len(set(prev_sel[b, h].tolist()) & set(sel[b, h].tolist()))
                     assert overlap >= ke - arrivals
         prev_sel, prev_st = sel, st.copy()
+
+
+# --------------------------------------------------------------------------------------
+# Decode append  ([P1] §3.1 pooled keys beside the cache; [P4] Method 1 block arrivals)
+# --------------------------------------------------------------------------------------
+
+def test_append_ramp_closed_form_and_skips():
+    # Token p of row (b, h) carries p + 1000 c + 1e5 (b H + h).  Appended one at a time with ragged
+    # lengths per sequence (a negative or past-the-end position leaves the sequence alone), every
+    # written slot (p // 64, p % 64) holds its token, every other slot keeps the sentinel, and the
+    # pooled keys of the finished sub-blocks are the ramp's mean in closed form.
+    B, H, nbmax, bs, d, sbs = 3, 2, 3, 64, 4, 16
+    lens = [0, 37, nbmax * bs]
+    ks = np.full((B, H, nbmax, bs, d), -5.0)
+    vs = np.full_like(ks, -5.0)
+    for p in range(nbmax * bs + 2):
+        pos = np.array([p if p < L else -1 for L in lens], dtype=np.int32)
+        if p == nbmax * bs + 1:
+            pos[2] = nbmax * bs          # past the end: skipped
+        kn = np.empty((B, H, d))
+        for b in range(B):
+            for h in range(H):
+                kn[b, h] = p + 1000.0 * np.arange(d) + 1e5 * (b * H + h)
+        O.append_kv(ks, vs, kn, -kn, pos)
+    for b, L in enumerate(lens):
+        for h in range(H):
+            flat = ks[b, h].reshape(nbmax * bs, d)
+            for p in range(nbmax * bs):
+                want = p + 1000.0 * np.arange(d) + 1e5 * (b * H + h) if p < L else np.full(d, -5.0)
+                assert np.array_equal(flat[p], want)
+                assert np.array_equal(vs[b, h].reshape(nbmax * bs, d)[p], -want if p < L else want)
+    kp = O.pool_keys(ks, sbs)
+    for b, L in enumerate(lens):
+        for h in range(H):
+            for j in range(L // sbs):
+                want = sbs * j + (sbs - 1) / 2 + 1000.0 * np.arange(d) + 1e5 * (b * H + h)
+                assert np.allclose(kp[b, h, j], want, rtol=0, atol=1e-9)
