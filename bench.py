@@ -145,7 +145,15 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
 
 
 def run_offload(steps_cap=None):
-    """C4: 128-step offload loop (pinned host KV pool, 64-slot cache per KV head)."""
+    """C4: 128-step offload loop (pinned host KV pool, 64-slot cache per KV head).
+
+    A step appends the previous step's token (nosa_append_kv into the pinned host pool and the
+    pooled keys), selects, and runs nosa_offload_decode (gather on a copy stream, overlapped with
+    attention over the cache hits).  Every pass starts from the same state (empty cache, prompt
+    pooled keys): one pass records miss counts and selections, three timed passes run the
+    overlapped path and three the serial calls (cache_update on the compute stream, then
+    sparse_decode), with events only around steps 1..steps-1; a last serial pass with events
+    between the calls gives the per-phase breakdown and the gather rate."""
     import numpy as np
     import torch
 
@@ -154,80 +162,135 @@ def run_offload(steps_cap=None):
 
     w = WORKLOADS["C4"]
     x = generate(w)
+    n0 = w.n_blocks
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
 
     def pin(a):
-        src = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        src = bf16(a)
         t = torch.empty(src.shape, dtype=torch.bfloat16, pin_memory=True)
         t.copy_(src)
         return t
 
-    hk, hv = pin(x["k"]), pin(x["v"])
-    kdev = torch.from_numpy(x["k"].view(np.int16)).view(torch.bfloat16).cuda()
+    prompt_k, prompt_v = x["k"].copy(), x["v"].copy()
+    prompt_k[:, :, n0:] = 0
+    prompt_v[:, :, n0:] = 0
+    hk, hv = pin(prompt_k), pin(prompt_v)
+    del prompt_k, prompt_v
+    kdev = bf16(x["k"]).cuda()
     shape0 = N.make_shape(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                           n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, cache_slots=w.cache_slots)
-    R, k, C = w.rows, w.k, w.cache_slots
-    kp = torch.empty((R, w.nbmax * 2, w.head_dim), dtype=torch.float32, device="cuda")
-    N.nosa_pool_keys(shape0, kdev, 0, w.nbmax, kp)
-    torch.cuda.synchronize()
-    del kdev
-    qs = torch.from_numpy(x["q_steps"].view(np.int16)).view(torch.bfloat16).cuda()
+    R, k, C, d = w.rows, w.k, w.cache_slots, w.head_dim
+    kp = torch.empty((R, w.nbmax * 2, d), dtype=torch.float32, device="cuda")
+    acc = torch.empty((R, d), dtype=torch.float32, device="cuda")
+    # the decode tokens, step-major: token t of the decode is position n_tokens + t
+    new_k = bf16(x["k"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, d).transpose(2, 0, 1, 3)).cuda()
+    new_v = bf16(x["v"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, d).transpose(2, 0, 1, 3)).cuda()
+    positions = (torch.arange(w.steps, dtype=torch.int32, device="cuda").view(-1, 1) + (w.n_tokens - 1)) \
+        .expand(w.steps, w.batch).contiguous()
+    qs = bf16(x["q_steps"]).cuda()
     ev = torch.from_numpy(x["evict"]).cuda()
     del x
-    ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, d), dtype=torch.bfloat16, device="cuda")
     cv = torch.zeros_like(ck)
-    sob = torch.full((R, w.nbmax), -1, dtype=torch.int32, device="cuda")
-    bos = torch.full((R, C), -1, dtype=torch.int32, device="cuda")
+    sob = torch.empty((R, w.nbmax), dtype=torch.int32, device="cuda")
+    bos = torch.empty((R, C), dtype=torch.int32, device="cuda")
     table = torch.empty((R, k), dtype=torch.int32, device="cuda")
     mcnt = torch.empty((R,), dtype=torch.int32, device="cuda")
     mlist = torch.empty((R, k, 2), dtype=torch.int32, device="cuda")
     agn = torch.empty((R, w.ke), dtype=torch.int32, device="cuda")
     sel = torch.empty((R, k), dtype=torch.int32, device="cuda")
-    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, d), dtype=torch.bfloat16, device="cuda")
     ws = N.workspace(shape0)
     stream = torch.cuda.current_stream()
     copy_stream = torch.cuda.Stream()
-    scale = 1.0 / (w.head_dim ** 0.5)
+    scale = 1.0 / (d ** 0.5)
     steps = w.steps if steps_cap is None else min(w.steps, steps_cap)
-    step_ms, gather_ms, misses, prev = [], [], [], None
-    gam = []
-    n_prev = 0
-    for t in range(steps):
-        n = visible_blocks(w, t)
-        shape = shape0.copy(n_blocks=n)
-        e0, e1, e2, e3 = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        e0.record(stream)
-        N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
-        N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, compute=stream,
-                            copy=copy_stream)
-        e1.record(stream)
-        N.nosa_sparse_decode(shape, qs[t], ck, cv, C, table, scale, out, ws, stream)
-        e2.record(stream)
+    mc_hist = torch.empty((steps, R), dtype=torch.int32, device="cuda")
+    sel_hist = torch.empty((steps, R, k), dtype=torch.int32, device="cuda")
+
+    def reset():
+        sob.fill_(-1)
+        bos.fill_(-1)
+        N.nosa_pool_keys(shape0, kdev, 0, n0, kp)
         torch.cuda.synchronize()
-        step_ms.append(e0.elapsed_time(e2))
-        gather_ms.append(e0.elapsed_time(e1))
-        mc = mcnt.cpu().numpy()
-        misses.append(int(mc.sum()))
-        s_h = sel.cpu().numpy()
-        if prev is not None:
-            inter = [len(set(a.tolist()) & set(b.tolist())) / k for a, b in zip(prev, s_h)]
-            gam.extend(inter)
-        prev = s_h
-        n_prev = n
+
+    def loop(overlap, timed=False, stats=False, phases=False):
+        """One pass of the loop from the reset state.  timed: events only after step 0 and after
+        the last step (warm mean over steps 1..); stats: copies of miss counts and selections per
+        step; phases: events between the calls of every step (each event adds a few us)."""
+        reset()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)] if phases else None
+        ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_prev = 0
+        for t in range(steps):
+            if timed and t == 1:
+                ta.record(stream)
+            n = visible_blocks(w, t)
+            shape = shape0.copy(n_blocks=n)
+            if phases:
+                evs[t][0].record(stream)
+            if t > 0:
+                N.nosa_append_kv(shape0, new_k[t - 1], new_v[t - 1], positions[t], hk, hv, acc, kp, stream)
+            N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
+            if phases:
+                evs[t][1].record(stream)
+            if overlap:
+                N.nosa_offload_decode(shape, qs[t], sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out,
+                                      ws, stream, copy_stream)
+            else:
+                N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, stream, stream)
+                if phases:
+                    evs[t][2].record(stream)
+                N.nosa_sparse_decode(shape, qs[t], ck, cv, C, table, scale, out, ws, stream)
+            if phases:
+                evs[t][3].record(stream)
+            if stats:
+                mc_hist[t].copy_(mcnt)
+                sel_hist[t].copy_(sel)
+            n_prev = n
+        if timed:
+            tb.record(stream)
+        torch.cuda.synchronize()
+        res = {}
+        if timed:
+            res["warm_ms"] = ta.elapsed_time(tb) / (steps - 1)
+        if phases:
+            res["select"] = [e[0].elapsed_time(e[1]) for e in evs]
+            res["cache"] = [e[1].elapsed_time(e[2]) for e in evs]
+            res["decode"] = [e[2].elapsed_time(e[3]) for e in evs]
+        return res
+
+    loop(True, stats=True)                        # warm-up pass (code objects, host pool pages) + stats
+    misses = mc_hist.sum(dim=1).cpu().numpy().tolist()
+    s_h = sel_hist.cpu().numpy()
+    mean_ms = statistics.median([loop(True, timed=True)["warm_ms"] for _ in range(3)])
+    serial_ms = statistics.median([loop(False, timed=True)["warm_ms"] for _ in range(3)])
+    ph = loop(False, phases=True)
+    gam = []
+    for t in range(1, steps):
+        gam.extend(len(set(a.tolist()) & set(b.tolist())) / k for a, b in zip(s_h[t - 1], s_h[t]))
     warm = slice(1, steps)
-    blk_bytes = 64 * w.head_dim * 2 * 2
+    blk_bytes = 64 * d * 2 * 2
     fetched = [m * blk_bytes for m in misses]
-    mean_ms = statistics.mean(step_ms[warm])
+    cache_ms = statistics.mean(ph["cache"][warm])
     return {
-        "workload": "C4: B16, GQA 32/8, d128, 16K ctx (+1 token/step), 32+32 blocks, 64-slot GPU cache per KV "
-                    "head, pinned host KV pool, %d steps" % steps,
+        "workload": "C4: B16, GQA 32/8, d128, 16K ctx (+1 token/step, appended to the pinned host pool), 32+32 "
+                    "blocks, 64-slot GPU cache per KV head, %d steps" % steps,
+        "path": "nosa_append_kv + nosa_select + nosa_offload_decode (gather on a copy stream, overlapped with "
+                "attention over the hits)",
         "hit_rate_warm": 1.0 - statistics.mean(misses[warm]) / (R * k),
         "fetched_bytes_per_step_warm": statistics.mean(fetched[warm]),
         "cold_step_fetched_bytes": fetched[0],
         "gamma_min": min(gam) if gam else None, "gamma_mean": statistics.mean(gam) if gam else None,
         "step_ms_mean_warm": mean_ms,
-        "select_cache_gather_ms_mean_warm": statistics.mean(gather_ms[warm]),
-        "h2d_gbps_warm": statistics.mean(fetched[warm]) / (statistics.mean(gather_ms[warm]) * 1e-3) / 1e9,
+        "serial_step_ms_mean_warm": serial_ms,
+        "serial_phase_ms_mean_warm": {"append_select": statistics.mean(ph["select"][warm]),
+                                      "cache_update": cache_ms, "sparse_decode": statistics.mean(ph["decode"][warm])},
+        "h2d_gbps_warm_serial_cache_update": statistics.mean(fetched[warm]) / (cache_ms * 1e-3) / 1e9,
         "tokens_per_s": w.batch / (mean_ms * 1e-3),
+        "tokens_per_s_serial": w.batch / (serial_ms * 1e-3),
     }
 
 

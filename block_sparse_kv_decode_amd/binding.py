@@ -27,7 +27,7 @@ NOSA_F32, NOSA_BF16 = 0, 1
 
 EXPORTED = (
     "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
-    "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode",
+    "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode", "nosa_offload_decode",
 )
 
 
@@ -90,6 +90,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_select.argtypes = [SP, P, P, P, I32, P, P, P, P]
     L.nosa_cache_update.restype = ctypes.c_int
     L.nosa_cache_update.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    L.nosa_offload_decode.restype = ctypes.c_int
+    L.nosa_offload_decode.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
     L.nosa_sparse_decode.restype = ctypes.c_int
     L.nosa_sparse_decode.argtypes = [SP, P, P, P, I32, P, ctypes.c_float, P, P, P]
     return L
@@ -175,3 +177,13 @@ def workspace(shape: NosaShape, device=None):
     """Zero-filled device workspace of nosa_workspace_bytes(shape) bytes (a torch uint8 tensor)."""
     import torch
     return torch.zeros(nosa_workspace_bytes(shape), dtype=torch.uint8, device=device or "cuda")
+
+
+def nosa_offload_decode(shape, q, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list,
+                        host_k, host_v, cache_k, cache_v, softmax_scale, out, ws, compute=None, copy=None) -> None:
+    """copy=None runs everything on the compute stream; pass a second stream to overlap the gather."""
+    cs = _stream(compute)
+    cp = cs if copy is None else _stream(copy)
+    _check(lib.nosa_offload_decode(ctypes.byref(shape), _p(q), _p(selected), _p(slot_of_block), _p(block_of_slot),
+                                   _p(block_table), _p(miss_cnt), _p(miss_list), _p(host_k), _p(host_v),
+                                   _p(cache_k), _p(cache_v), ctypes.c_float(softmax_scale), _p(out), _p(ws), cs, cp))

@@ -142,7 +142,7 @@ PartPlan select_plan(const nosa_shape *s) {
 }
 
 struct WsLayout {
-    size_t scores, part, total;
+    size_t scores, part, tab_hit, total;
 };
 
 WsLayout ws_layout(const nosa_shape *s) {
@@ -152,8 +152,14 @@ WsLayout ws_layout(const nosa_shape *s) {
     size_t off = 0;
     L.scores = off;
     off = round_up(off + R * (size_t)s->n_blocks_max * sizeof(float), kAlign);
+    // With a cache configured, nosa_offload_decode fills 2 S partial slots per row (hits, then
+    // misses) and keeps the hit-only table beside them.
+    const bool offload = s->cache_slots >= s->kq + s->ke;
     L.part = off;
-    off = round_up(off + R * (size_t)dp.S * group_of(s) * (size_t)(s->head_dim + 2) * sizeof(float), kAlign);
+    off = round_up(off + R * (size_t)(offload ? 2 : 1) * dp.S * group_of(s) * (size_t)(s->head_dim + 2) * sizeof(float),
+                   kAlign);
+    L.tab_hit = off;
+    if (offload) off = round_up(off + R * (size_t)(s->kq + s->ke) * sizeof(int32_t), kAlign);
     L.total = off;
     return L;
 }
@@ -340,17 +346,22 @@ int nosa_select(const nosa_shape *shape, const void *q, const float *pooled_k, c
     return run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream);
 }
 
-int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
+// Validation and launches shared by nosa_cache_update and nosa_offload_decode.  With a distinct
+// copy stream the gather runs there, after the map (event), and *copied is set to an event that
+// marks its end; the caller makes the compute stream wait on it.
+static int cache_step(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
                       int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
-                      const void *host_k, const void *host_v, void *cache_k, void *cache_v, hipStream_t compute,
-                      hipStream_t copy) {
-    int rc = check_shape(shape);
-    if (rc) return rc;
+                      const void *host_k, const void *host_v, void *cache_k, void *cache_v, int32_t *table_hit,
+                      hipStream_t compute, hipStream_t copy, hipEvent_t *copied) {
+    *copied = nullptr;
     const int k = shape->kq + shape->ke;
     if (shape->cache_slots < k)
         return fail(NOSA_ECAPACITY, "cache_slots %d is below the budget kq + ke = %d", shape->cache_slots, k);
     if (shape->cache_slots > kMaxBlocks)
         return fail(NOSA_EUNSUPPORTED, "cache_slots %d exceeds %d", shape->cache_slots, kMaxBlocks);
+    if (rows_of(shape) > kGatherMaxRows)
+        return fail(NOSA_EUNSUPPORTED, "batch x n_kv_heads = %d exceeds %d for the cache", rows_of(shape),
+                    kGatherMaxRows);
     REQUIRE_PTR(selected, 4);
     REQUIRE_PTR(slot_of_block, 4);
     REQUIRE_PTR(block_of_slot, 4);
@@ -382,6 +393,7 @@ int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t 
     c.table = block_table;
     c.mcnt = miss_cnt;
     c.mlist = miss_list;
+    c.table_hit = table_hit;
     c.k = k;
     c.C = shape->cache_slots;
     c.nbmax = shape->n_blocks_max;
@@ -395,23 +407,112 @@ int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t 
     g.cv = (unsigned char *)cache_v;
     g.mcnt = miss_cnt;
     g.mlist = miss_list;
+    g.rows = R;
     g.k = k;
     g.C = shape->cache_slots;
     g.nbmax = shape->n_blocks_max;
     g.block_bytes = (long long)shape->block_size * shape->head_dim * (long long)elem_bytes(shape);
 
     if (copy == nullptr || copy == compute) {
-        e = launch_gather(g, R, compute);
-        return e == hipSuccess ? ok() : hip_fail(e, "gather launch");
+        e = launch_gather(g, compute);
+        return e == hipSuccess ? NOSA_OK : hip_fail(e, "gather launch");
     }
     DeviceEvents *ev = nullptr;
+    int rc;
     if ((rc = get_events(&ev)) != NOSA_OK) return rc;
     if ((e = hipEventRecord(ev->mapped, compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(copy, ev->mapped, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    if ((e = launch_gather(g, R, copy)) != hipSuccess) return hip_fail(e, "gather launch");
+    if ((e = launch_gather(g, copy)) != hipSuccess) return hip_fail(e, "gather launch");
     if ((e = hipEventRecord(ev->copied, copy)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = hipStreamWaitEvent(compute, ev->copied, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    *copied = ev->copied;
+    return NOSA_OK;
+}
+
+static int check_decode_args(const void *q, const void *k_store, const void *v_store, int32_t store_blocks,
+                             float softmax_scale, const void *out, const void *ws) {
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(k_store, 16);
+    REQUIRE_PTR(v_store, 16);
+    REQUIRE_PTR(out, 16);
+    REQUIRE_PTR(ws, kAlign);
+    if (store_blocks < 1) return fail(NOSA_EINVAL, "store_blocks must be >= 1 (got %d)", store_blocks);
+    if (!(softmax_scale > 0.0f) || softmax_scale != softmax_scale)
+        return fail(NOSA_EINVAL, "softmax_scale must be a positive finite number");
+    return NOSA_OK;
+}
+
+static DecodeArgs decode_args(const nosa_shape *shape, const void *q, const void *k_store, const void *v_store,
+                              int32_t store_blocks, float softmax_scale, void *out, void *ws) {
+    const WsLayout L = ws_layout(shape);
+    const SplitPlan sp = decode_plan(shape);
+    DecodeArgs a;
+    a.q = q;
+    a.k = k_store;
+    a.v = v_store;
+    a.table = nullptr;
+    a.out = out;
+    a.part = (float *)((char *)ws + L.part);
+    a.count = nullptr;
+    a.Hq = shape->n_q_heads;
+    a.Hkv = shape->n_kv_heads;
+    a.k_sel = shape->kq + shape->ke;
+    a.store_blocks = store_blocks;
+    a.tab_stride = 1;
+    a.S = sp.S;
+    a.nbs = sp.nbs;
+    a.St = sp.S;
+    a.s0 = 0;
+    a.direct = sp.S == 1;
+    a.sl2 = softmax_scale * 1.4426950408889634f;
+    return a;
+}
+
+int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
+                      int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
+                      const void *host_k, const void *host_v, void *cache_k, void *cache_v, hipStream_t compute,
+                      hipStream_t copy) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    hipEvent_t copied = nullptr;
+    rc = cache_step(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k, host_v,
+                    cache_k, cache_v, nullptr, compute, copy, &copied);
+    if (rc) return rc;
+    if (copied) {
+        hipError_t e = hipStreamWaitEvent(compute, copied, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    }
     return ok();
+}
+
+int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *selected, int32_t *slot_of_block,
+                        int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
+                        const void *host_k, const void *host_v, void *cache_k, void *cache_v, float softmax_scale,
+                        void *out, void *ws, hipStream_t compute, hipStream_t copy) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_decode_args(q, cache_k, cache_v, shape->cache_slots, softmax_scale, out, ws)) != NOSA_OK) return rc;
+    const WsLayout L = ws_layout(shape);
+    int32_t *tab_hit = (int32_t *)((char *)ws + L.tab_hit);
+    hipEvent_t copied = nullptr;
+    rc = cache_step(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k, host_v,
+                    cache_k, cache_v, tab_hit, compute, copy, &copied);
+    if (rc) return rc;
+    // hits: attended while the misses are in transit (partial slots [0, S))
+    DecodeArgs a = decode_args(shape, q, cache_k, cache_v, shape->cache_slots, softmax_scale, out, ws);
+    a.table = tab_hit;
+    a.St = 2 * a.S;
+    a.direct = 0;
+    const int G = group_of(shape), R = rows_of(shape);
+    hipError_t e = launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, false);
+    if (e != hipSuccess) return hip_fail(e, "offload_decode hit launch");
+    if (copied && (e = hipStreamWaitEvent(compute, copied, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    // misses: their cache slots straight from the miss list (slots [S, 2S)), then one merge
+    a.table = miss_list + 1;
+    a.tab_stride = 2;
+    a.count = miss_cnt;
+    a.s0 = a.S;
+    e = launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, true);
+    return e == hipSuccess ? ok() : hip_fail(e, "offload_decode miss launch");
 }
 
 int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store, const void *v_store,
@@ -419,32 +520,11 @@ int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_sto
                        hipStream_t stream) {
     int rc = check_shape(shape);
     if (rc) return rc;
-    REQUIRE_PTR(q, 16);
-    REQUIRE_PTR(k_store, 16);
-    REQUIRE_PTR(v_store, 16);
     REQUIRE_PTR(block_table, 4);
-    REQUIRE_PTR(out, 16);
-    REQUIRE_PTR(ws, kAlign);
-    if (store_blocks < 1) return fail(NOSA_EINVAL, "store_blocks must be >= 1 (got %d)", store_blocks);
-    if (!(softmax_scale > 0.0f) || softmax_scale != softmax_scale)
-        return fail(NOSA_EINVAL, "softmax_scale must be a positive finite number");
-    const WsLayout L = ws_layout(shape);
-    const SplitPlan sp = decode_plan(shape);
-    DecodeArgs a;
-    a.q = q;
-    a.k = k_store;
-    a.v = v_store;
+    if ((rc = check_decode_args(q, k_store, v_store, store_blocks, softmax_scale, out, ws)) != NOSA_OK) return rc;
+    DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
     a.table = block_table;
-    a.out = out;
-    a.part = (float *)((char *)ws + L.part);
-    a.Hq = shape->n_q_heads;
-    a.Hkv = shape->n_kv_heads;
-    a.k_sel = shape->kq + shape->ke;
-    a.store_blocks = store_blocks;
-    a.S = sp.S;
-    a.nbs = sp.nbs;
-    a.sl2 = softmax_scale * 1.4426950408889634f;
-    hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream);
+    hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream, true);
     return e == hipSuccess ? ok() : hip_fail(e, "sparse_decode launch");
 }
 

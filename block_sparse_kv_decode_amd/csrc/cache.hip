@@ -11,9 +11,9 @@
 //   ascending block id with a ballot prefix count; free slots (empty, or holding a block not
 //   selected now) are ranked in ascending slot order from an LDS bitmap of hit slots; the i-th
 //   miss takes the i-th free slot.  Deterministic, no global atomics.
-// gather: grid (row, miss index); a workgroup copies one K block and one V block from the
-//   device-mapped pinned host pool into the cache slot with 16-byte loads, or exits at once when
-//   its index is past the row's miss count.
+// gather: a small persistent grid walks the flattened miss list; for each miss a workgroup copies
+//   one K block and one V block from the device-mapped pinned host pool into the cache slot with
+//   16-byte loads.
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
@@ -47,6 +47,7 @@ __global__ __launch_bounds__(64) void cache_map_kernel(CacheArgs a) {
         const bool hit = inr && slot >= 0 && slot < C;
         if (hit) held[slot] = 1;
         if (valid) table[i] = hit ? slot : -1;
+        if (valid && a.table_hit) a.table_hit[(size_t)row * k + i] = hit ? slot : -1;
         const bool miss = inr && !hit;
         const uint64_t mm = __ballot(miss);
         if (miss) {
@@ -86,29 +87,71 @@ __global__ __launch_bounds__(64) void cache_map_kernel(CacheArgs a) {
 }
 
 constexpr int kGatherThreads = 256;
+#ifndef NOSA_GATHER_WORKGROUPS
+#define NOSA_GATHER_WORKGROUPS 32
+#endif
+// A few workgroups, each with 16 KiB of host reads in flight, keep the link busy.  Many more
+// (one per miss) would park megabytes of slow host reads in the memory queues, where they hold up
+// the HBM traffic of the attention kernel that runs beside the gather.
+constexpr int kGatherWorkgroups = NOSA_GATHER_WORKGROUPS;
 
-// Block bytes are 64 tokens x d x element size, always a multiple of 2 x 256 x 16 bytes, so every
-// thread moves whole pairs of 16-byte chunks of K and of V (four loads in flight per thread).
+// Persistent gather.  Every workgroup scans the per-row miss counts into LDS, then walks the
+// flattened miss list (row-major, rank within the row) with stride gridDim.x, finding the row of
+// item t by binary search in the scanned counts.  Block bytes are 64 tokens x d x element size,
+// always a multiple of 2 x 256 x 16 bytes: each thread moves pairs of 16-byte chunks of K and of V
+// (four loads in flight per thread).
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
-    const int row = blockIdx.x / a.k, r = blockIdx.x - row * a.k;
-    if (r >= a.mcnt[row]) return;
-    const int blk = a.mlist[((size_t)row * a.k + r) * 2 + 0];
-    const int slot = a.mlist[((size_t)row * a.k + r) * 2 + 1];
-    if ((unsigned)blk >= (unsigned)a.nbmax || (unsigned)slot >= (unsigned)a.C) return;
-    const size_t src = ((size_t)row * a.nbmax + blk) * (size_t)a.block_bytes;
-    const size_t dst = ((size_t)row * a.C + slot) * (size_t)a.block_bytes;
-    const uint4 *hk = (const uint4 *)(a.hk + src);
-    const uint4 *hv = (const uint4 *)(a.hv + src);
-    uint4 *ck = (uint4 *)(a.ck + dst);
-    uint4 *cv = (uint4 *)(a.cv + dst);
+    __shared__ int start[kGatherMaxRows + 1];   // start[row] = misses of rows before it
+    __shared__ int wsum[kGatherThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int carry = 0;
+    for (int base = 0; base < a.rows; base += kGatherThreads) {
+        const int row = base + tid;
+        const int c = row < a.rows ? min(max(a.mcnt[row], 0), a.k) : 0;
+        int x = c;                                   // inclusive scan inside the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wsum[w] = x;
+        __syncthreads();
+        int before = carry;
+        for (int ww = 0; ww < w; ++ww) before += wsum[ww];
+        if (row < a.rows) start[row] = before + x - c;
+        int tot = 0;
+        for (int ww = 0; ww < kGatherThreads / 64; ++ww) tot += wsum[ww];
+        carry += tot;
+        __syncthreads();
+    }
+    if (tid == 0) start[a.rows] = carry;
+    __syncthreads();
+    const int total = carry;
     const int n16 = (int)(a.block_bytes / 16);
-    for (int i = threadIdx.x; i < n16; i += 2 * kGatherThreads) {
-        const uint4 k0 = hk[i], k1 = hk[i + kGatherThreads];
-        const uint4 v0 = hv[i], v1 = hv[i + kGatherThreads];
-        ck[i] = k0;
-        ck[i + kGatherThreads] = k1;
-        cv[i] = v0;
-        cv[i + kGatherThreads] = v1;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        int lo = 0, hi = a.rows - 1;                 // last row with start[row] <= t
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (start[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        const int row = lo, r = t - start[row];
+        const int blk = a.mlist[((size_t)row * a.k + r) * 2 + 0];
+        const int slot = a.mlist[((size_t)row * a.k + r) * 2 + 1];
+        if ((unsigned)blk >= (unsigned)a.nbmax || (unsigned)slot >= (unsigned)a.C) continue;
+        const size_t src = ((size_t)row * a.nbmax + blk) * (size_t)a.block_bytes;
+        const size_t dst = ((size_t)row * a.C + slot) * (size_t)a.block_bytes;
+        const uint4 *hk = (const uint4 *)(a.hk + src);
+        const uint4 *hv = (const uint4 *)(a.hv + src);
+        uint4 *ck = (uint4 *)(a.ck + dst);
+        uint4 *cv = (uint4 *)(a.cv + dst);
+        for (int i = tid; i < n16; i += 2 * kGatherThreads) {
+            const uint4 k0 = hk[i], k1 = hk[i + kGatherThreads];
+            const uint4 v0 = hv[i], v1 = hv[i + kGatherThreads];
+            ck[i] = k0;
+            ck[i + kGatherThreads] = k1;
+            cv[i] = v0;
+            cv[i + kGatherThreads] = v1;
+        }
     }
 }
 
@@ -122,8 +165,8 @@ hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs &a, int rows, hipStream_t st) {
-    gather_kernel<<<dim3((unsigned)(rows * a.k)), dim3(kGatherThreads), 0, st>>>(a);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t st) {
+    gather_kernel<<<dim3((unsigned)kGatherWorkgroups), dim3(kGatherThreads), 0, st>>>(a);
     return hipGetLastError();
 }
 

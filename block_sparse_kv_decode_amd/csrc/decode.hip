@@ -25,8 +25,12 @@
 //   Prefetch : K and V of the next blocks are loaded into registers while a block is computed
 //              (two blocks ahead for bf16, one for fp32).
 // End of split: lane reduction, a 4-wave merge through LDS, then either the final output
-// (S = 1) or a (max, sum, acc) partial in the workspace, merged by combine_kernel with the same
-// online-softmax rule.  No workgroup waits on another.
+// (one split) or a (max, sum, acc) partial in the workspace, merged by combine_kernel with the same
+// online-softmax rule.  No workgroup waits on another.  A launch may fill only some of a row's
+// partial slots (slots [s0, s0 + S) of St): the offload step attends the cache hits in one launch
+// while the missed blocks are still in transit, and the missed blocks in a second launch that
+// reads their slots straight from the miss list (entry stride 2, per-row count), and one combine
+// merges both.
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
@@ -143,16 +147,18 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, int row, int s
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sh.m[ww][h]);
         float L = 0.0f, A = 0.0f;
+        if (M != -INFINITY) {     // else the split saw no block: empty partial (M = -inf, L = A = 0)
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = fast_exp2(sh.m[ww][h] - M);
-            L = fmaf(sh.l[ww][h], f, L);
-            A = fmaf(sh.acc[ww][h][dd], f, A);
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = fast_exp2(sh.m[ww][h] - M);
+                L = fmaf(sh.l[ww][h], f, L);
+                A = fmaf(sh.acc[ww][h][dd], f, A);
+            }
         }
-        if (a.S == 1) {
+        if (a.direct) {
             store_elem<T>(a.out, out_base + idx, A / L);
         } else {
-            float *part = a.part + ((size_t)(row * a.S + sp) * G + h) * (D + 2);
+            float *part = a.part + ((size_t)(row * a.St + a.s0 + sp) * G + h) * (D + 2);
             part[2 + dd] = A;
             if (dd == 0) {
                 part[0] = M;
@@ -178,7 +184,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int j16 = lane & 15, grp = lane >> 4;       // MFMA layout: column (head) / k-group
     const int cpv = lane % NC, tpv = lane / NC;       // PV layout
-    const int j0 = sp * a.nbs, j1 = min(a.k_sel, j0 + a.nbs);
+    const int n_use = a.count ? min(a.k_sel, a.count[row]) : a.k_sel;
+    const int j0 = sp * a.nbs, j1 = min(n_use, j0 + a.nbs);
 
     // B operand: q of head j16 (zero columns beyond G), dims 32 ks + 8 grp .. + 8
     bf16x8_t qb[KS];
@@ -258,9 +265,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         wave_lds_sync();
     };
 
-    const int32_t *tab = a.table + (size_t)row * a.k_sel;
+    const int32_t *tab = a.table + (size_t)row * a.k_sel * a.tab_stride;
     auto load = [&](int j, uint4(&kk)[KS], uint4(&vv)[CPL]) -> bool {
-        const int blk = tab[j];
+        const int blk = tab[(size_t)j * a.tab_stride];
         if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
         const char *kp = kbase + (size_t)blk * blk_bytes;
         const char *vp = vbase + (size_t)blk * blk_bytes;
@@ -314,7 +321,8 @@ __global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_k
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int sub = lane & 3, tq = lane >> 2;          // QK layout: 4 lanes per key row
     const int cpv = lane % NC, tpv = lane / NC;        // PV layout
-    const int j0 = sp * a.nbs, j1 = min(a.k_sel, j0 + a.nbs);
+    const int n_use = a.count ? min(a.k_sel, a.count[row]) : a.k_sel;
+    const int j0 = sp * a.nbs, j1 = min(n_use, j0 + a.nbs);
 
     uint4 qf[G][CPL];
     {
@@ -394,9 +402,9 @@ __global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_k
         wave_lds_sync();
     };
 
-    const int32_t *tab = a.table + (size_t)row * a.k_sel;
+    const int32_t *tab = a.table + (size_t)row * a.k_sel * a.tab_stride;
     auto load = [&](int j, uint4(&kk)[CPL], uint4(&vv)[CPL]) -> bool {
-        const int blk = tab[j];
+        const int blk = tab[(size_t)j * a.tab_stride];
         if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
         const char *kp = kbase + (size_t)blk * blk_bytes;
         const char *vp = vbase + (size_t)blk * blk_bytes;
@@ -432,19 +440,22 @@ __global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_k
     finish_split<float, D, G>(a, row, sp, m_h, l_h, acc, sh);
 }
 
-// Merges the S split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
+// Merges the St split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
+// Empty partials (max = -inf) carry nothing and are passed over.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
     const int row = blockIdx.x / G, h = blockIdx.x - row * G;
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int dd = threadIdx.x;
-    const float *rp = a.part + ((size_t)row * a.S * G + h) * (D + 2);
+    const float *rp = a.part + ((size_t)row * a.St * G + h) * (D + 2);
     const size_t stride = (size_t)G * (D + 2);
     float M = -INFINITY, L = 0.0f, A = 0.0f;
 #pragma unroll 4
-    for (int s = 0; s < a.S; ++s) {
+    for (int s = 0; s < a.St; ++s) {
         const float *ps = rp + s * stride;
-        const float ms = ps[0], ls = ps[1], as = ps[2 + dd];
+        const float ms = ps[0];
+        if (ms == -INFINITY) continue;
+        const float ls = ps[1], as = ps[2 + dd];
         const float mn = fmaxf(M, ms);
         const float fo = fast_exp2(M - mn), fn = fast_exp2(ms - mn);
         L = L * fo + ls * fn;
@@ -455,30 +466,33 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
 }
 
 template <typename T, int D, int G>
-static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st) {
+static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st, bool merge) {
     if (sizeof(T) == 2)
         decode_mfma_kernel<D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
     else
         decode_valu_kernel<D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.S == 1) return e;
+    if (e != hipSuccess || a.direct || !merge) return e;
     combine_kernel<T, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_d(int G, const DecodeArgs &a, int rows, hipStream_t st) {
+static hipError_t launch_decode_d(int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge) {
     switch (G) {
-        case 1: return launch_decode_t<T, D, 1>(a, rows, st);
-        case 2: return launch_decode_t<T, D, 2>(a, rows, st);
-        case 4: return launch_decode_t<T, D, 4>(a, rows, st);
-        default: return launch_decode_t<T, D, 8>(a, rows, st);
+        case 1: return launch_decode_t<T, D, 1>(a, rows, st, merge);
+        case 2: return launch_decode_t<T, D, 2>(a, rows, st, merge);
+        case 4: return launch_decode_t<T, D, 4>(a, rows, st, merge);
+        default: return launch_decode_t<T, D, 8>(a, rows, st, merge);
     }
 }
 
-hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st) {
-    if (dtype == 1) return d == 128 ? launch_decode_d<uint16_t, 128>(G, a, rows, st) : launch_decode_d<uint16_t, 64>(G, a, rows, st);
-    return d == 128 ? launch_decode_d<float, 128>(G, a, rows, st) : launch_decode_d<float, 64>(G, a, rows, st);
+// merge: run combine_kernel over the St partial slots after this launch (unless direct).
+hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge) {
+    if (dtype == 1)
+        return d == 128 ? launch_decode_d<uint16_t, 128>(G, a, rows, st, merge)
+                        : launch_decode_d<uint16_t, 64>(G, a, rows, st, merge);
+    return d == 128 ? launch_decode_d<float, 128>(G, a, rows, st, merge) : launch_decode_d<float, 64>(G, a, rows, st, merge);
 }
 
 }  // namespace nosa

@@ -53,6 +53,7 @@ struct CacheArgs {
     int32_t *table;       // [R, k]
     int32_t *mcnt;        // [R]
     int32_t *mlist;       // [R, k, 2]
+    int32_t *table_hit;   // optional [R, k]: table with the misses as -1
     int k, C, nbmax;
 };
 
@@ -61,19 +62,24 @@ struct GatherArgs {
     unsigned char *ck, *cv;         // cache [R, C, block_bytes]
     const int32_t *mcnt;
     const int32_t *mlist;
-    int k, C, nbmax;
+    int rows, k, C, nbmax;
     long long block_bytes;
 };
+constexpr int kGatherMaxRows = 8192;   // rows (batch x KV heads) one cache update can serve
 
 struct DecodeArgs {
     const void *q;        // [B, Hq, d]
     const void *k, *v;    // [R, store_blocks, 64, d]
-    const int32_t *table; // [R, k_sel]
+    const int32_t *table; // row r's entries: table[(r * k_sel + j) * tab_stride], j < k_sel
     void *out;            // [B, Hq, d]
-    float *part;          // [R, S, G, d + 2] split partials (S > 1)
+    float *part;          // [R, St, G, d + 2] split partials (max, sum, acc)
+    const int32_t *count; // optional [R]: row r uses its first count[r] entries (NULL: all k_sel)
     int Hq, Hkv, k_sel, store_blocks;
-    int S;                // splits per row
+    int tab_stride;       // int32 elements from one table entry to the next (1, or 2 for a miss list)
+    int S;                // splits per row in this launch
     int nbs;              // blocks per split
+    int St, s0;           // partial slots per row; first slot written by this launch
+    int direct;           // 1: single split, write the output itself (no partials)
     float sl2;            // softmax scale * log2(e)
 };
 
@@ -84,7 +90,7 @@ hipError_t launch_append(int dtype, int d, const AppendArgs &a, int rows, hipStr
 hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads, hipStream_t st);
 size_t select_lds_bytes(int n_blocks);
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
-hipError_t launch_gather(const GatherArgs &a, int rows, hipStream_t st);
-hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t st);
+hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge);
 
 }  // namespace nosa

@@ -13,6 +13,8 @@
  *   3. (offloaded KV only) hit/miss check against the GPU block cache, replacement map and
  *      host-to-GPU copy of the missed blocks                  -> nosa_cache_update ([P1] §4, App. A)
  *   4. GQA attention over the tokens of the selected blocks  -> nosa_sparse_decode ([P1] App. A)
+ *   3+4 fused for offloaded KV, with the copy of the missed blocks overlapped with attention over
+ *      the blocks already cached                             -> nosa_offload_decode ([P1] §4, App. A)
  * Pooled keys (sub-block means) are state kept next to the KV cache -> nosa_pool_keys ([P1] §3.1),
  * extended token by token by the decode append path -> nosa_append_kv.
  *
@@ -30,7 +32,7 @@
  *     eviction scores and block scores are float32.  Accumulation is float32 everywhere.
  *   - Supported set: head_dim 64 or 128; block_size 64; sub_block_size 8, 16, 32 or 64;
  *     n_q_heads / n_kv_heads in {1, 2, 4, 8}; 1 <= kq + ke <= n_blocks <= n_blocks_max <= 16384;
- *     cache_slots >= kq + ke (for nosa_cache_update).  Anything else returns NOSA_EUNSUPPORTED
+ *     cache_slots >= kq + ke (for nosa_cache_update and nosa_offload_decode).  Anything else returns NOSA_EUNSUPPORTED
  *     or NOSA_EINVAL.
  *   - Workspace: nosa_workspace_bytes() bytes of device memory, 256-byte aligned, no initial
  *     contents required (it holds block scores and split-K partials between the kernels of one
@@ -84,8 +86,9 @@ const char *nosa_last_error(void);
 /* Library build identifier (compile target and version string). */
 const char *nosa_version(void);
 
-/* Device workspace bytes needed by nosa_select / nosa_block_scores / nosa_sparse_decode for this
- * shape (the same workspace serves all three).  Returns 0 if the shape is invalid (see
+/* Device workspace bytes needed by nosa_select / nosa_block_scores / nosa_sparse_decode /
+ * nosa_offload_decode for this shape (the same workspace serves all four; it is larger when
+ * cache_slots >= kq + ke, for the offload path).  Returns 0 if the shape is invalid (see
  * nosa_last_error). */
 size_t nosa_workspace_bytes(const nosa_shape *shape);
 
@@ -218,6 +221,27 @@ int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t 
 int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store,
                        const void *v_store, int32_t store_blocks, const int32_t *block_table,
                        float softmax_scale, void *out, void *ws, hipStream_t stream);
+
+/*
+ * Offloaded decode step after selection: nosa_cache_update, then nosa_sparse_decode over the GPU
+ * cache, with the host-to-GPU copy of the missed blocks overlapped with attention over the hit
+ * blocks ([P1] §4: cached blocks are used in place and only missed blocks are moved; App. A: the
+ * step is selection, transfer, attention).  On `compute`: the map kernel, then attention over the
+ * hits; on `copy` (when it is a distinct stream): the gather of the misses; `compute` then waits for
+ * the gather, attends the missed blocks and merges the two parts with the online-softmax rule.
+ * With copy NULL or equal to compute everything runs on compute, in order.
+ * All arguments are those of nosa_cache_update and nosa_sparse_decode (store_blocks =
+ * cache_slots, table = block_table).  slot_of_block, block_of_slot, block_table, miss_cnt,
+ * miss_list and the cache contents come out exactly as from nosa_cache_update; `out` equals the
+ * nosa_sparse_decode result up to float32 summation order (the split partials are grouped by
+ * hit / miss).  The workspace must come from nosa_workspace_bytes of a shape with
+ * cache_slots >= kq + ke.  Errors as for the two calls.
+ */
+int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *selected,
+                        int32_t *slot_of_block, int32_t *block_of_slot, int32_t *block_table,
+                        int32_t *miss_cnt, int32_t *miss_list, const void *host_k, const void *host_v,
+                        void *cache_k, void *cache_v, float softmax_scale, void *out, void *ws,
+                        hipStream_t compute, hipStream_t copy);
 
 #ifdef __cplusplus
 }

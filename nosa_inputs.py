@@ -100,7 +100,9 @@ WORKLOADS: Dict[str, Workload] = {
                    description="single step: B16, GQA 32/8, d128, 16K ctx, 32+32 blocks, bf16"),
     "C3": Workload("C3", 64, 32, 8, 128, 4096, 8, 8, "bf16", seed=3,
                    description="single step: B64, GQA 32/8, d128, 4K ctx, 8+8 blocks, bf16"),
-    "C4": Workload("C4", 16, 32, 8, 128, 16384, 32, 32, "bf16", seed=4, n_blocks_max=257,
+    # 258 blocks allocated: block 256 fills during the first 64 decode steps, and the tokens of
+    # steps 65..127 go to block 257, which is still open (never visible) when the loop ends.
+    "C4": Workload("C4", 16, 32, 8, 128, 16384, 32, 32, "bf16", seed=4, n_blocks_max=258,
                    cache_slots=64, steps=128, drift_sigma=0.3,
                    description="offload loop: C2 shape, 128 steps, 64-slot GPU cache, pinned host pool"),
     "C5": Workload("C5", 4, 32, 8, 128, 131072, 32, 32, "bf16", seed=5,

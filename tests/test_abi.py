@@ -141,3 +141,20 @@ def test_one_hip_runtime_in_the_process():
             "print(len(m)); print(m)\n")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True, cwd=ROOT).stdout
     assert out.splitlines()[0] == "1", out
+
+
+def test_offload_decode_rejects_on_host():
+    s = _good(cache_slots=10)
+    args = [16] * 11
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_offload_decode(s, 16, *args[:10], 0.1, 16, 256, compute=0, copy=0)
+    assert ei.value.code == N.NOSA_ECAPACITY
+    s = _good()
+    with pytest.raises(N.NosaError) as ei:      # miss_list NULL
+        N.nosa_offload_decode(s, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, 16, 0.1, 16, 256, compute=0, copy=0)
+    assert ei.value.code == N.NOSA_EINVAL
+    with pytest.raises(N.NosaError) as ei:      # bad scale
+        N.nosa_offload_decode(s, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, 256, compute=0, copy=0)
+    assert ei.value.code == N.NOSA_EINVAL
+    # the workspace grows by the hit table and the second set of partial slots when a cache is set
+    assert N.nosa_workspace_bytes(_good(cache_slots=64)) > N.nosa_workspace_bytes(_good(cache_slots=0))

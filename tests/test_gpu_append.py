@@ -70,9 +70,10 @@ def test_append_tokens_ragged(dtype, d, sbs, pinned_store):
 
 def test_append_decode_loop_blocks_arrive_from_host_pool():
     # Prompt of 6 blocks, then 3 blocks' worth of decode tokens appended into the pinned host pool.
-    # Each step selects over the complete blocks (a block becomes visible the step after its last
-    # token lands, as an arrival for the query-agnostic subset), updates the cache from the host
-    # pool and attends.  Selections, maps and attention follow the oracle at every step.
+    # At step t >= 1 the token of step t-1 (position 6*64 + t - 1) is appended first; a block is
+    # visible from the step its last token lands, as an arrival for the query-agnostic subset.
+    # Each step selects over the complete blocks, updates the cache from the host pool and attends.
+    # Selections, maps and attention follow the oracle.
     w = small_workload("append_loop", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=6,
                        n_blocks_max=9, kq=2, ke=3, seed=42, cache_slots=7)
     x = generate(w)
@@ -101,37 +102,35 @@ def test_append_decode_loop_blocks_arrive_from_host_pool():
     rng = np.random.default_rng(7)
     qf = x["q"]
     agn, agn_ref, n_prev, arrivals = None, None, 0, 0
-    steps = 3 * BS
+    steps = 3 * BS + 1
     for t in range(steps):
-        pos = n0 * BS + t
-        # the step's new token joins the host pool and the pooled keys first
-        N.nosa_append_kv(shape0, H.dev(_token(x["k"], pos)), H.dev(_token(x["v"], pos)),
-                         torch.full((w.batch,), pos, dtype=torch.int32, device="cuda"), hk, hv, acc, kp)
-        n = pos // BS          # complete blocks before this token; the open block is not a candidate
+        if t > 0:
+            pos = n0 * BS + t - 1
+            N.nosa_append_kv(shape0, H.dev(_token(x["k"], pos)), H.dev(_token(x["v"], pos)),
+                             torch.full((w.batch,), pos, dtype=torch.int32, device="cuda"), hk, hv, acc, kp)
+        n = (n0 * BS + t) // BS
         shape = shape0.copy(n_blocks=n)
         q_dev = H.dev(qf)
         sel, agn_new = H.gpu_select(shape, q_dev, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
         N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv)
         out = H.gpu_decode(shape, q_dev, ck, cv, C, table, ws)
         torch.cuda.synchronize()
-        arrivals += int(n > n_prev and t > 0)
-        check = t in (0, 1, 63, 64, 65, 128, 129, steps - 1) or n != n_prev
+        arrivals += int(t > 0 and n > n_prev)
+        check = t in (0, 1, 63, 65, 127, 129, steps - 2) or (t > 0 and n != n_prev)
         sel_h = H.host(sel)
         tab_ref, mc_ref, ml_ref = O.cache_step(sel_h, sob_ref, bos_ref)
         assert np.array_equal(H.host(table), tab_ref) and np.array_equal(H.host(mcnt), mc_ref)
+        s_ref = O.block_scores(qf, kp_ref[:, :, :2 * n], n, 2)
         if check:
-            s_ref = O.block_scores(qf, kp_ref[:, :, :2 * n], n, 2)
             H.check_selection(sel_h, H.host(agn_new), s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
             ref = O.attention(qf, x["k"], x["v"], sel_h.reshape(w.batch, w.n_kv_heads, k))
             H.check_attention(H.host(out), ref, "bf16", "append loop step %d" % t)
             # the pooled keys of every complete block match the oracle's
             kph = H.host(kp).reshape(w.batch, w.n_kv_heads, -1, d)
             np.testing.assert_allclose(kph[:, :, :2 * n], kp_ref[:, :, :2 * n], rtol=1e-6, atol=1e-6)
-        _, agn_ref, _ = O.select(O.block_scores(qf, kp_ref[:, :, :2 * n], n, 2), x["evict"], w.kq, w.ke, n_prev,
-                                 agn_ref)
+        _, agn_ref, _ = O.select(s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
         agn, n_prev = agn_new, n
         qf = f32_to_bf16_bits((H.as_f64(qf) + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32))
-    assert arrivals == 2
+    assert arrivals == 3 and n_prev == nbmax
     # the host pool holds every appended token
-    hkh = H.host(hk)
-    assert np.array_equal(hkh[:, :, :n0 + 3], x["k"][:, :, :n0 + 3])
+    assert np.array_equal(H.host(hk), x["k"]) and np.array_equal(H.host(hv), x["v"])

@@ -1,7 +1,9 @@
 """Full-size parity on the configured workloads, in the launch configuration the benchmark
 times (automatic splits and parts): C2 (B16, 16K ctx), C3 (B64, 4K ctx), C5 (B4, 128K ctx)
-end to end against the oracle element by element, and the C4 offload loop (128 steps) with
-per-step invariants and oracle checks on sampled steps."""
+end to end against the oracle element by element, and the C4 offload loop (128 steps, decode
+tokens appended through nosa_append_kv, the gather overlapped with attention by
+nosa_offload_decode on a copy stream) with per-step invariants and oracle checks on sampled
+steps."""
 
 import numpy as np
 import pytest
@@ -46,8 +48,21 @@ def test_c4_offload_loop():
     x = generate(w)
     shape0 = H.shape_of(w)
     R, k, C = w.rows, w.k, w.cache_slots
-    hk, hv = H.pinned(x["k"]), H.pinned(x["v"])
-    kp = H.gpu_pool(shape0, H.dev(x["k"]))          # pooled keys: setup, from a device copy
+    n0 = w.n_blocks
+    # The host pool and the pooled keys start with the prompt; the decode tokens join them through
+    # nosa_append_kv, one per step.
+    prompt_k, prompt_v = x["k"].copy(), x["v"].copy()
+    prompt_k[:, :, n0:] = 0
+    prompt_v[:, :, n0:] = 0
+    hk, hv = H.pinned(prompt_k), H.pinned(prompt_v)
+    del prompt_k, prompt_v
+    kp = torch.full((R, w.nbmax * 2, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    N.nosa_pool_keys(shape0, H.dev(x["k"]), 0, n0, kp)      # reads blocks [0, n0) only
+    acc = torch.zeros((R, w.head_dim), dtype=torch.float32, device="cuda")
+    kn_all = H.dev(np.ascontiguousarray(x["k"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
+                                         .transpose(2, 0, 1, 3)))
+    vn_all = H.dev(np.ascontiguousarray(x["v"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
+                                         .transpose(2, 0, 1, 3)))
     torch.cuda.synchronize()
     ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, w.head_dim), dtype=torch.bfloat16, device="cuda")
     cv = torch.zeros_like(ck)
@@ -60,6 +75,7 @@ def test_c4_offload_loop():
     ev_dev = H.dev(x["evict"])
     q_all = H.dev(x["q_steps"])
     copy_stream = torch.cuda.Stream()
+    scale = 1.0 / np.sqrt(w.head_dim)
     kp_ref = None
     sampled = {0, 1, 63, 64, 65, w.steps - 1}
     agn = None
@@ -73,10 +89,15 @@ def test_c4_offload_loop():
             torch.cuda.synchronize()
             snap = {"agn": None if agn is None else H.host(agn).copy(), "sob": H.host(sob).copy(),
                     "bos": H.host(bos).copy()}
+        if t > 0:
+            pos = w.n_tokens + t - 1
+            N.nosa_append_kv(shape0, kn_all[t - 1], vn_all[t - 1],
+                             torch.full((w.batch,), pos, dtype=torch.int32, device="cuda"), hk, hv, acc, kp)
         q_t = q_all[t]
         sel, agn = H.gpu_select(shape, q_t, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
-        N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, copy=copy_stream)
-        out = H.gpu_decode(shape, q_t, ck, cv, C, table, ws)
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        N.nosa_offload_decode(shape, q_t, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out, ws,
+                              copy=copy_stream)
         torch.cuda.synchronize()
         sel_h = H.host(sel)
         mc = H.host(mcnt)
@@ -113,6 +134,11 @@ def test_c4_offload_loop():
         n_prev = n
         if t % 32 == 0:
             print("C4 step %d ok" % t, flush=True)
+    # pooled keys built by the appends: bit-identical to pooling the full store at once
+    torch.cuda.synchronize()
+    n_end = visible_blocks(w, w.steps - 1)
+    kp_once = H.gpu_pool(shape0, H.dev(x["k"]))
+    assert torch.equal(kp[:, :2 * n_end].view(torch.int32), kp_once[:, :2 * n_end].view(torch.int32))
     g = np.concatenate(gammas)
     print("C4 gamma min %.3f mean %.3f; hit rate (warm) %.3f" % (g.min(), g.mean(), np.mean(hits[1:]) / k))
     assert g.min() >= w.ke / k - 1e-12

@@ -342,3 +342,90 @@ def test_select_sink_window(n, kq, ke, ns, nw, parts):
         for r in range(B * Hkv):
             assert set(range(ns)) | set(range(cur - nw, cur)) <= set(E[r].tolist())
         prev = cur
+
+
+@pytest.mark.parametrize("dtype,d,G,side_stream", [("bf16", 128, 4, True), ("bf16", 128, 4, False),
+                                                   ("f32", 64, 2, True), ("bf16", 64, 8, True)])
+def test_offload_decode_matches_cache_update_then_decode(dtype, d, G, side_stream):
+    # nosa_offload_decode (hits attended while the misses are copied, then the misses, one merge)
+    # against nosa_cache_update + nosa_sparse_decode run on a second copy of the state: maps, table,
+    # miss list and cache bytes identical, attention within tolerance of the oracle at every step.
+    # Step 0 is cold (every entry a miss: the hit launch has only empty splits); later steps mix.
+    w = small_workload("offload2", batch=2, n_q_heads=2 * G, n_kv_heads=2, head_dim=d, n_blocks=40,
+                       n_blocks_max=44, kq=6, ke=6, seed=36, cache_slots=15, dtype=dtype)
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    R, k, C = w.rows, w.k, w.cache_slots
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    hk, hv = H.pinned(x["k"]), H.pinned(x["v"])
+
+    def state():
+        ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, d), dtype=tdt, device="cuda")
+        return dict(ck=ck, cv=torch.zeros_like(ck),
+                    sob=torch.full((R, w.nbmax), -1, dtype=torch.int32, device="cuda"),
+                    bos=torch.full((R, C), -1, dtype=torch.int32, device="cuda"),
+                    table=torch.full((R, k), -9, dtype=torch.int32, device="cuda"),
+                    mcnt=torch.full((R,), -9, dtype=torch.int32, device="cuda"),
+                    mlist=torch.full((R, k, 2), -9, dtype=torch.int32, device="cuda"))
+    A, B = state(), state()
+    kp_dev = H.gpu_pool(shape0, H.dev(x["k"]))
+    ws_a, ws_b = N.workspace(shape0), N.workspace(shape0)
+    ev_dev = H.dev(x["evict"])
+    copy_stream = torch.cuda.Stream() if side_stream else None
+    scale = 1.0 / np.sqrt(d)
+    rng = np.random.default_rng(8)
+    qf = x["q"]
+    n, agn = 40, None
+    from nosa_inputs import f32_to_bf16_bits
+    for t in range(8):
+        n_prev = 0 if t == 0 else n
+        if t in (2, 5):
+            n += 1
+        shape = shape0.copy(n_blocks=n)
+        q_dev = H.dev(qf)
+        sel, agn = H.gpu_select(shape, q_dev, kp_dev, ev_dev, ws_a, n_prev=n_prev, agn=agn)
+        N.nosa_cache_update(shape, sel, A["sob"], A["bos"], A["table"], A["mcnt"], A["mlist"], hk, hv, A["ck"],
+                            A["cv"])
+        out_a = H.gpu_decode(shape, q_dev, A["ck"], A["cv"], C, A["table"], ws_a, scale)
+        out_b = torch.full_like(out_a, float("nan"))
+        N.nosa_offload_decode(shape, q_dev, sel, B["sob"], B["bos"], B["table"], B["mcnt"], B["mlist"], hk, hv,
+                              B["ck"], B["cv"], scale, out_b, ws_b, copy=copy_stream)
+        torch.cuda.synchronize()
+        mc = H.host(A["mcnt"])
+        for key in ("sob", "bos", "table", "mcnt", "ck", "cv"):
+            assert torch.equal(A[key].view(torch.int16) if A[key].dtype == torch.bfloat16 else A[key],
+                               B[key].view(torch.int16) if B[key].dtype == torch.bfloat16 else B[key]), (t, key)
+        mla, mlb = H.host(A["mlist"]), H.host(B["mlist"])
+        for r in range(R):
+            assert np.array_equal(mla[r, :mc[r]], mlb[r, :mc[r]])
+        if t == 0:
+            assert np.all(mc == k)            # cold cache: every entry misses
+        sel_h = H.host(sel).reshape(w.batch, w.n_kv_heads, k)
+        ref = O.attention(qf, x["k"], x["v"], sel_h, scale)
+        H.check_attention(H.host(out_b), ref, dtype, "offload_decode step %d" % t)
+        H.check_attention(H.host(out_a), ref, dtype, "cache_update + sparse_decode step %d" % t)
+        if dtype == "bf16":
+            qf = f32_to_bf16_bits((H.as_f64(qf) + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32))
+        else:
+            qf = (qf + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32)
+
+
+def test_sparse_decode_split_with_no_valid_block():
+    # A split whose every table entry is skipped contributes an empty partial, not a NaN: the
+    # result equals attention over the remaining valid entries.
+    w = small_workload("empty_split", batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=32, kq=8, ke=8,
+                       seed=37)
+    x = generate(w)
+    shape = H.shape_of(w, decode_splits=4)
+    table = np.tile(np.arange(16, dtype=np.int32), (2, 1))
+    table[:, 4:8] = -1                  # split 1 (entries 4..7) has nothing to attend
+    table[1, 12:16] = 999               # and split 3 of row 1: out of range, skipped
+    ws = N.workspace(shape)
+    out = H.gpu_decode(shape, H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), w.nbmax, H.dev(table), ws)
+    torch.cuda.synchronize()
+    keep = [[i for i in range(16) if table[r, i] >= 0 and table[r, i] < w.nbmax] for r in range(2)]
+    for r in range(2):
+        sub = np.array(keep[r], dtype=np.int32)
+        ref = O.attention(x["q"][:, 4 * r:4 * r + 4].copy(), x["k"][:, r:r + 1].copy(), x["v"][:, r:r + 1].copy(),
+                          sub.reshape(1, 1, -1))
+        H.check_attention(H.host(out)[:, 4 * r:4 * r + 4], ref, "bf16", "row %d" % r)
