@@ -268,6 +268,39 @@ def run_offload(steps_cap=None):
     mean_ms = statistics.median([loop(True, timed=True)["warm_ms"] for _ in range(3)])
     serial_ms = statistics.median([loop(False, timed=True)["warm_ms"] for _ in range(3)])
     ph = loop(False, phases=True)
+    # A serving loop waits for every step.  Host wall time per step with a synchronisation after
+    # each, the step's calls launched eagerly vs replayed from captured HIP graphs (inputs copied
+    # into static buffers first in both cases).
+    from block_sparse_kv_decode_amd.step_graph import OffloadStepGraphs
+    st = dict(host_k=hk, host_v=hv, pooled_k=kp, pool_acc=acc, evict=ev, agn=agn, selected=sel, slot_of_block=sob,
+              block_of_slot=bos, block_table=table, miss_cnt=mcnt, miss_list=mlist, cache_k=ck, cache_v=cv, out=out,
+              ws=ws)
+    graphs = OffloadStepGraphs(shape0, st, copy_stream, scale)
+
+    def sync_loop(use_graph):
+        reset()
+        wall = []
+        n_prev = 0
+        for t in range(steps):
+            n = visible_blocks(w, t)
+            t0 = time.perf_counter()
+            graphs.q.copy_(qs[t])
+            if t > 0:
+                graphs.k_new.copy_(new_k[t - 1])
+                graphs.v_new.copy_(new_v[t - 1])
+                graphs.positions.copy_(positions[t])
+            if use_graph:
+                graphs.replay(n, n_prev, t > 0)
+            else:
+                graphs.enqueue(n, n_prev, t > 0)
+            torch.cuda.synchronize()
+            wall.append((time.perf_counter() - t0) * 1e3)
+            n_prev = n
+        return statistics.median(wall[1:])
+
+    sync_loop(True)                               # captures the graphs
+    sync_eager_ms = statistics.median([sync_loop(False) for _ in range(3)])
+    sync_graph_ms = statistics.median([sync_loop(True) for _ in range(3)])
     gam = []
     for t in range(1, steps):
         gam.extend(len(set(a.tolist()) & set(b.tolist())) / k for a, b in zip(s_h[t - 1], s_h[t]))
@@ -291,6 +324,8 @@ def run_offload(steps_cap=None):
         "h2d_gbps_warm_serial_cache_update": statistics.mean(fetched[warm]) / (cache_ms * 1e-3) / 1e9,
         "tokens_per_s": w.batch / (mean_ms * 1e-3),
         "tokens_per_s_serial": w.batch / (serial_ms * 1e-3),
+        "sync_every_step_wall_ms_median": {"eager": sync_eager_ms, "hip_graph": sync_graph_ms,
+                                           "graphs_captured": len(graphs.graphs)},
     }
 
 
