@@ -5,13 +5,14 @@ nosa_select (pooled-key block scoring + query-agnostic / query-aware selection) 
 nosa_sparse_decode (split-K GQA attention over the selected blocks).  Pooled keys are state
 built once before timing (they change only when a block fills up).  tokens/s = batch / step time.
 
-  python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--config C2] [--also C3]
-                  [--no-cpu-baseline] [--offload]
+  python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--config C2] [--also C3,F1]
+                  [--no-cpu-baseline] [--no-offload] [--no-transfer]
 
 Prints one JSON line.  `value` is the headline workload (bs16 / 16K context by default); the
-same line carries the bs64 / 4K workload under "also", the decode kernel's roofline and the
-CPU oracle baseline.  --offload adds the 128-step offload loop (pinned host KV pool, 64-slot
-GPU cache) under "offload".
+same line carries the bs64 / 4K workload and the sink + window split under "also", the decode
+kernel's roofline and the CPU oracle baseline, the 128-step offload loop (pinned host KV pool,
+64-slot GPU cache, decode tokens appended each step) under "offload", and the block- vs
+element-wise transfer sweep under "transfer_granularity".
 """
 
 from __future__ import annotations
@@ -329,6 +330,62 @@ def run_offload(steps_cap=None):
     }
 
 
+def run_transfer(reps=20):
+    """Block-wise vs element-wise host-to-GPU transfer at batch 64, 4096-token context, d 128 bf16,
+    2 KV heads (128 rows).  Per row a 1024-token (16-block) GPU cache; at locality gamma a fraction
+    1 - gamma of it is refilled per step, either as whole 64-token blocks (16 KiB units) or as
+    single tokens (256-byte units) scattered over the row's context, K and V each.  Both moves carry
+    the same bytes through nosa_gather_units; lists are in ascending source order."""
+    import numpy as np
+    import torch
+
+    import block_sparse_kv_decode_amd as N
+
+    R, ctx, cache_tok, d, bs = 64 * 2, 4096, 1024, 128, 64
+    tok_b, blk_b = d * 2, bs * d * 2
+    host_k = torch.empty(R * ctx * d, dtype=torch.bfloat16, pin_memory=True).fill_(1.0)
+    host_v = torch.empty(R * ctx * d, dtype=torch.bfloat16, pin_memory=True).fill_(2.0)
+    dev_k = torch.zeros(R * cache_tok * d, dtype=torch.bfloat16, device="cuda")
+    dev_v = torch.zeros_like(dev_k)
+    rng = np.random.default_rng(11)
+    stream = torch.cuda.current_stream()
+    out = []
+
+    def timed(unit_bytes, su, du, n_src, n_dst):
+        su_t, du_t = torch.from_numpy(su).cuda(), torch.from_numpy(du).cuda()
+        n = len(su)
+        for _ in range(3):
+            N.nosa_gather_units(host_k, n_src, dev_k, n_dst, unit_bytes, su_t, du_t, n, stream)
+            N.nosa_gather_units(host_v, n_src, dev_v, n_dst, unit_bytes, su_t, du_t, n, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            N.nosa_gather_units(host_k, n_src, dev_k, n_dst, unit_bytes, su_t, du_t, n, stream)
+            N.nosa_gather_units(host_v, n_src, dev_v, n_dst, unit_bytes, su_t, du_t, n, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for gamma in (0.5, 0.8, 0.9, 0.95, 0.99):
+        nb = max(1, int(round((1 - gamma) * (cache_tok // bs) * R)))
+        dst = rng.choice(R * (cache_tok // bs), nb, replace=False)
+        src = (dst // (cache_tok // bs)) * (ctx // bs) + rng.integers(0, ctx // bs, nb)
+        o = np.argsort(src, kind="stable")
+        t_blk = timed(blk_b, src[o].astype(np.int32), dst[o].astype(np.int32), R * (ctx // bs), R * (cache_tok // bs))
+        nt = nb * bs
+        dst = rng.choice(R * cache_tok, nt, replace=False)
+        src = (dst // cache_tok) * ctx + rng.integers(0, ctx, nt)
+        o = np.argsort(src, kind="stable")
+        t_tok = timed(tok_b, src[o].astype(np.int32), dst[o].astype(np.int32), R * ctx, R * cache_tok)
+        by = 2 * nb * blk_b
+        out.append({"gamma": gamma, "bytes_per_step": by, "block_units": 2 * nb, "element_units": 2 * nt,
+                    "block_ms": t_blk, "element_ms": t_tok,
+                    "block_gbps": by / (t_blk * 1e-3) / 1e9, "element_gbps": by / (t_tok * 1e-3) / 1e9})
+    return {"workload": "batch 64, context 4096, d 128 bf16, 2 KV heads: a 1024-token GPU cache per row, "
+                        "refilled by a fraction 1 - gamma per step (K and V)",
+            "block_unit_bytes": blk_b, "element_unit_bytes": tok_b, "by_locality": out}
+
+
 def measure_link_peak():
     """Pinned host -> device copy bandwidth of a large hipMemcpyAsync (SDMA), GB/s."""
     import torch
@@ -400,7 +457,8 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--also", default="C3,F1", help="comma list of extra resident workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--offload", action="store_true", help="also run the 128-step offload loop")
+    ap.add_argument("--no-offload", action="store_true", help="skip the 128-step offload loop (C4)")
+    ap.add_argument("--no-transfer", action="store_true", help="skip the block- vs element-wise transfer sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -472,9 +530,14 @@ def main():
         }
     if also:
         line["also"] = also
-    if args.offload:
+    link = None
+    if not args.no_offload:
         line["offload"] = run_offload()
-        line["offload"]["link_peak_gbps_sdma"] = measure_link_peak()
+        link = measure_link_peak()
+        line["offload"]["link_peak_gbps_sdma"] = link
+    if not args.no_transfer:
+        line["transfer_granularity"] = run_transfer()
+        line["transfer_granularity"]["link_peak_gbps_sdma"] = link if link is not None else measure_link_peak()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config)
     print(json.dumps(line), flush=True)

@@ -28,6 +28,7 @@ NOSA_F32, NOSA_BF16 = 0, 1
 EXPORTED = (
     "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
     "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode", "nosa_offload_decode",
+    "nosa_gather_units",
 )
 
 
@@ -90,6 +91,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_select.argtypes = [SP, P, P, P, I32, P, P, P, P]
     L.nosa_cache_update.restype = ctypes.c_int
     L.nosa_cache_update.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    L.nosa_gather_units.restype = ctypes.c_int
+    L.nosa_gather_units.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int64, P]
     L.nosa_offload_decode.restype = ctypes.c_int
     L.nosa_offload_decode.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
     L.nosa_sparse_decode.restype = ctypes.c_int
@@ -187,3 +190,9 @@ def nosa_offload_decode(shape, q, selected, slot_of_block, block_of_slot, block_
     _check(lib.nosa_offload_decode(ctypes.byref(shape), _p(q), _p(selected), _p(slot_of_block), _p(block_of_slot),
                                    _p(block_table), _p(miss_cnt), _p(miss_list), _p(host_k), _p(host_v),
                                    _p(cache_k), _p(cache_v), ctypes.c_float(softmax_scale), _p(out), _p(ws), cs, cp))
+
+
+def nosa_gather_units(src, src_units, dst, dst_units, unit_bytes, src_unit, dst_unit, n_units,
+                      stream=None) -> None:
+    _check(lib.nosa_gather_units(_p(src), int(src_units), _p(dst), int(dst_units), int(unit_bytes), _p(src_unit),
+                                 _p(dst_unit), int(n_units), _stream(stream)))

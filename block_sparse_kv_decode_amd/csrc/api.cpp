@@ -286,6 +286,36 @@ int nosa_append_kv(const nosa_shape *shape, const void *k_new, const void *v_new
     return e == hipSuccess ? ok() : hip_fail(e, "append_kv launch");
 }
 
+int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst_units, int64_t unit_bytes,
+                      const int32_t *src_unit, const int32_t *dst_unit, int64_t n_units, hipStream_t stream) {
+    if (unit_bytes < 16 || unit_bytes > (1 << 20) || (unit_bytes & (unit_bytes - 1)) != 0)
+        return fail(NOSA_EINVAL, "unit_bytes must be a power of two in [16, 1 MiB] (got %lld)", (long long)unit_bytes);
+    if (n_units < 0) return fail(NOSA_EINVAL, "n_units must be >= 0 (got %lld)", (long long)n_units);
+    if (src_units < 0 || dst_units < 0) return fail(NOSA_EINVAL, "buffer sizes must be >= 0");
+    if (n_units == 0) return ok();
+    REQUIRE_PTR(src, 16);
+    REQUIRE_PTR(dst, 16);
+    REQUIRE_PTR(src_unit, 4);
+    REQUIRE_PTR(dst_unit, 4);
+    void *ds = nullptr, *dd = nullptr;
+    int rc;
+    if ((rc = device_address(src, &ds, "src")) != NOSA_OK) return rc;
+    if ((rc = device_address(dst, &dd, "dst")) != NOSA_OK) return rc;
+    UnitsArgs a;
+    a.src = (const unsigned char *)ds;
+    a.dst = (unsigned char *)dd;
+    a.src_unit = src_unit;
+    a.dst_unit = dst_unit;
+    a.n_units = n_units;
+    a.n_src = src_units;
+    a.n_dst = dst_units;
+    int sh = 0;
+    while ((16ll << sh) < unit_bytes) ++sh;
+    a.chunk_shift = sh;
+    hipError_t e = launch_gather_units(a, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "gather_units launch");
+}
+
 static int run_scores(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
                       int32_t n_prev, int32_t *agn_state, int32_t *selected, float *scores_out, void *ws,
                       hipStream_t stream) {

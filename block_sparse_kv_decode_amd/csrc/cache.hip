@@ -155,6 +155,49 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
     }
 }
 
+// Transfer at any granularity: unit u of the source (src_unit[u] * unit_bytes bytes in) goes to
+// unit dst_unit[u] of the destination.  The flattened (unit, 16-byte chunk) index space is walked
+// with a grid stride, four chunks in flight per thread; unit_bytes is a power of two, so the unit
+// and the chunk come from a shift and a mask.  With 16 KiB units this is the block gather's
+// traffic pattern; with the 256 bytes of one token's key (or value) it is an element-wise gather.
+constexpr int kUnitsThreads = 256;
+constexpr int kUnitsWorkgroups = 32;
+
+__global__ __launch_bounds__(kUnitsThreads) void gather_units_kernel(UnitsArgs a) {
+    const long long total = a.n_units << a.chunk_shift;
+    const long long stride = (long long)gridDim.x * kUnitsThreads;
+    const long long cmask = (1ll << a.chunk_shift) - 1;
+    for (long long i0 = (long long)blockIdx.x * kUnitsThreads + threadIdx.x; i0 < total; i0 += 4 * stride) {
+        uint4 x[4];
+        long long dsto[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const long long i = i0 + j * stride;
+            dsto[j] = -1;
+            if (i < total) {
+                const long long u = i >> a.chunk_shift, c = i & cmask;
+                const int su = a.src_unit[u], du = a.dst_unit[u];
+                if (su >= 0 && su < a.n_src && du >= 0 && du < a.n_dst) {   // out-of-range units are skipped
+                    dsto[j] = ((long long)du << a.chunk_shift) + c;
+                    x[j] = ((const uint4 *)a.src)[((long long)su << a.chunk_shift) + c];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (dsto[j] >= 0) ((uint4 *)a.dst)[dsto[j]] = x[j];
+    }
+}
+
+hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st) {
+    if (a.n_units == 0) return hipSuccess;
+    const long long chunks = a.n_units << a.chunk_shift;
+    long long wgs = (chunks + kUnitsThreads * 4 - 1) / (kUnitsThreads * 4);
+    if (wgs > kUnitsWorkgroups) wgs = kUnitsWorkgroups;
+    gather_units_kernel<<<dim3((unsigned)wgs), dim3(kUnitsThreads), 0, st>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st) {
     const size_t dyn = (size_t)((a.C + 15) & ~15) + 3 * sizeof(int) * (size_t)a.k;
     if (dyn > 48 * 1024) {

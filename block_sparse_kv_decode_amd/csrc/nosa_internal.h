@@ -67,6 +67,15 @@ struct GatherArgs {
 };
 constexpr int kGatherMaxRows = 8192;   // rows (batch x KV heads) one cache update can serve
 
+struct UnitsArgs {
+    const unsigned char *src;       // device address (device memory or mapped pinned host memory)
+    unsigned char *dst;
+    const int32_t *src_unit, *dst_unit;
+    long long n_units;
+    long long n_src, n_dst;         // units in the source / destination buffers
+    int chunk_shift;                // log2(unit_bytes / 16)
+};
+
 struct DecodeArgs {
     const void *q;        // [B, Hq, d]
     const void *k, *v;    // [R, store_blocks, 64, d]
@@ -91,6 +100,7 @@ hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int row
 size_t select_lds_bytes(int n_blocks);
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t st);
+hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st);
 hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge);
 
 }  // namespace nosa

@@ -223,6 +223,26 @@ int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_sto
                        float softmax_scale, void *out, void *ws, hipStream_t stream);
 
 /*
+ * Transfer at a chosen granularity ([P1] §3.2: block-wise against element-wise communication;
+ * [P1] §4: the transfer kernel reads pinned host memory through unified virtual addressing).
+ * For u < n_units: bytes [src_unit[u] * unit_bytes, +unit_bytes) of src are copied to
+ * [dst_unit[u] * unit_bytes, +unit_bytes) of dst.  With unit_bytes = one KV block per head
+ * (16 KiB at 64 tokens x d 128 x bf16) this is the block gather of nosa_cache_update; with the
+ * bytes of one token's key or value it is an element-wise gather.
+ *   src, src_units : pinned host memory (read through its device mapping) or device memory,
+ *               holding src_units units
+ *   dst, dst_units : device memory (or pinned host memory) holding dst_units units
+ *   unit_bytes: power of two in [16, 1 MiB]
+ *   src_unit, dst_unit : device, [n_units] int32 unit indices; a pair with either index outside
+ *               its buffer is skipped; dst_unit entries must be distinct (else which copy lands is
+ *               undefined)
+ * n_units == 0 is a no-op.  Errors: NOSA_EINVAL for a bad size, a NULL or misaligned pointer, or
+ * memory that is neither device memory nor pinned host memory.
+ */
+int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst_units, int64_t unit_bytes,
+                      const int32_t *src_unit, const int32_t *dst_unit, int64_t n_units, hipStream_t stream);
+
+/*
  * Offloaded decode step after selection: nosa_cache_update, then nosa_sparse_decode over the GPU
  * cache, with the host-to-GPU copy of the missed blocks overlapped with attention over the hit
  * blocks ([P1] §4: cached blocks are used in place and only missed blocks are moved; App. A: the

@@ -223,6 +223,21 @@ def append_kv(k_store: np.ndarray, v_store: np.ndarray, k_new: np.ndarray, v_new
         v_store[b, :, p // bs, p % bs, :] = v_new[b]
 
 
+def gather_units(src: np.ndarray, dst: np.ndarray, unit_bytes: int, src_unit: np.ndarray,
+                 dst_unit: np.ndarray) -> None:
+    """Transfer at a chosen granularity, in place ([P1] paperlayer.ai summary §3.2, block-wise
+    against element-wise communication).  src and dst are viewed as arrays of unit_bytes-byte
+    units; for each pair u, unit src_unit[u] of src is copied to unit dst_unit[u] of dst, and a pair
+    with either index outside its buffer is skipped."""
+    s8 = np.ascontiguousarray(src).view(np.uint8).reshape(-1)
+    assert dst.flags["C_CONTIGUOUS"]
+    d8 = dst.view(np.uint8).reshape(-1)
+    ns, nd = s8.size // unit_bytes, d8.size // unit_bytes
+    for su, du in zip(np.asarray(src_unit).tolist(), np.asarray(dst_unit).tolist()):
+        if 0 <= su < ns and 0 <= du < nd:
+            d8[du * unit_bytes:(du + 1) * unit_bytes] = s8[su * unit_bytes:(su + 1) * unit_bytes]
+
+
 def locality(prev: np.ndarray, cur: np.ndarray, nbmax: int) -> np.ndarray:
     """gamma per row = |prev ∩ cur| / k."""
     k = cur.shape[-1]

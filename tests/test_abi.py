@@ -158,3 +158,17 @@ def test_offload_decode_rejects_on_host():
     assert ei.value.code == N.NOSA_EINVAL
     # the workspace grows by the hit table and the second set of partial slots when a cache is set
     assert N.nosa_workspace_bytes(_good(cache_slots=64)) > N.nosa_workspace_bytes(_good(cache_slots=0))
+
+
+def test_gather_units_rejects_on_host():
+    for ub in (0, 8, 24, 1 << 21):
+        with pytest.raises(N.NosaError) as ei:
+            N.nosa_gather_units(16, 4, 16, 4, ub, 16, 16, 1, stream=0)
+        assert ei.value.code == N.NOSA_EINVAL
+    with pytest.raises(N.NosaError):
+        N.nosa_gather_units(16, 4, 16, 4, 256, 16, 16, -1, stream=0)
+    with pytest.raises(N.NosaError):
+        N.nosa_gather_units(None, 4, 16, 4, 256, 16, 16, 1, stream=0)
+    with pytest.raises(N.NosaError):
+        N.nosa_gather_units(16, 4, 8, 4, 256, 16, 16, 1, stream=0)        # dst misaligned
+    N.nosa_gather_units(None, 0, None, 0, 256, None, None, 0, stream=0)   # zero units: no-op

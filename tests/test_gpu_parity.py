@@ -429,3 +429,29 @@ def test_sparse_decode_split_with_no_valid_block():
         ref = O.attention(x["q"][:, 4 * r:4 * r + 4].copy(), x["k"][:, r:r + 1].copy(), x["v"][:, r:r + 1].copy(),
                           sub.reshape(1, 1, -1))
         H.check_attention(H.host(out)[:, 4 * r:4 * r + 4], ref, "bf16", "row %d" % r)
+
+
+@pytest.mark.parametrize("unit_bytes,pinned_src", [(16, False), (256, True), (256, False), (16384, True)])
+def test_gather_units_matches_oracle(unit_bytes, pinned_src):
+    # Random transfer lists (distinct destinations, some pairs out of range) at the granularity of a
+    # 16-byte chunk, one token's key row (256 B) and one KV block (16 KiB): the destination matches
+    # the oracle byte for byte, untouched units included.
+    rng = np.random.default_rng(unit_bytes)
+    ns, nd = 3000 if unit_bytes < 16384 else 96, 2000 if unit_bytes < 16384 else 64
+    n = nd // 2
+    src = rng.integers(0, 2 ** 31, size=ns * unit_bytes // 4, dtype=np.int64).astype(np.int32)
+    dst0 = rng.integers(0, 2 ** 31, size=nd * unit_bytes // 4, dtype=np.int64).astype(np.int32)
+    su = rng.integers(0, ns, size=n).astype(np.int32)
+    du = rng.permutation(nd)[:n].astype(np.int32)
+    su[::97] = ns + 5                 # out of range: skipped
+    du[5::101] = -1
+    ref = dst0.copy()
+    O.gather_units(src, ref, unit_bytes, su, du)
+    s_t = H.pinned(src) if pinned_src else H.dev(src)
+    d_t = H.dev(dst0)
+    N.nosa_gather_units(s_t, ns, d_t, nd, unit_bytes, H.dev(su), H.dev(du), n)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.host(d_t), ref)
+    N.nosa_gather_units(s_t, ns, d_t, nd, unit_bytes, H.dev(su), H.dev(du), 0)   # no-op
+    torch.cuda.synchronize()
+    assert np.array_equal(H.host(d_t), ref)

@@ -487,3 +487,46 @@ def test_append_ramp_closed_form_and_skips():
             for j in range(L // sbs):
                 want = sbs * j + (sbs - 1) / 2 + 1000.0 * np.arange(d) + 1e5 * (b * H + h)
                 assert np.allclose(kp[b, h, j], want, rtol=0, atol=1e-9)
+
+
+# --------------------------------------------------------------------------------------
+# Transfer granularity  ([P1] §3.2 block-wise vs element-wise; §4 fine-grained block transfer)
+# --------------------------------------------------------------------------------------
+
+def test_gather_units_hand_example():
+    # 16-byte units of a byte ramp: unit i holds bytes 16 i .. 16 i + 15.
+    src = np.arange(8 * 16, dtype=np.uint8)
+    dst = np.full(5 * 16, 255, dtype=np.uint8)
+    O.gather_units(src, dst, 16, np.array([3, 0, 7, 9, 2]), np.array([1, 4, 0, 2, 7]))
+    want = np.full(5 * 16, 255, dtype=np.uint8)
+    want[16:32] = np.arange(48, 64)       # unit 3 -> 1
+    want[64:80] = np.arange(0, 16)        # unit 0 -> 4
+    want[0:16] = np.arange(112, 128)      # unit 7 -> 0
+    # (9 -> 2) source out of range, (2 -> 7) destination out of range: both skipped
+    assert np.array_equal(dst, want)
+
+
+def test_gather_units_block_granularity_equals_block_gather():
+    # With one KV block as the unit, the unit transfer reproduces the block gather of the cache
+    # update for the same miss list (two independent implementations of one copy).
+    rng = np.random.default_rng(3)
+    B, H, nb, C, bs, d = 2, 2, 6, 4, 64, 8
+    host = rng.integers(0, 65535, size=(B, H, nb, bs, d), dtype=np.uint16)
+    cache_a = np.zeros((B, H, C, bs, d), np.uint16)
+    cache_b = np.zeros_like(cache_a)
+    mcnt = np.array([[2, 0], [3, 1]], np.int32)
+    ml = np.full((B, H, 4, 2), -1, np.int32)
+    ml[0, 0, :2] = [[5, 1], [0, 3]]
+    ml[1, 0, :3] = [[1, 0], [2, 2], [4, 1]]
+    ml[1, 1, :1] = [[3, 3]]
+    O.gather(mcnt, ml, host, cache_a)
+    ub = bs * d * 2
+    su, du = [], []
+    for b in range(B):
+        for h in range(H):
+            r = b * H + h
+            for i in range(mcnt[b, h]):
+                su.append(r * nb + ml[b, h, i, 0])
+                du.append(r * C + ml[b, h, i, 1])
+    O.gather_units(host, cache_b, ub, np.array(su), np.array(du))
+    assert np.array_equal(cache_a, cache_b)
