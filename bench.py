@@ -69,6 +69,48 @@ def algorithmic_bytes(w):
     return {"step": kv_sel + kp + ev + q + o + ids, "decode": decode, "select": select}
 
 
+class HipTimingEvents:
+    """HIP timing events created with hipEventDisableSystemFence.  A default event performs a
+    system-scope fence (cache writeback and invalidation) when it completes, which lengthens and
+    disturbs the kernels it brackets; timing-only events can skip it.  The calls go to the HIP
+    runtime torch has loaded (found in the process map, so no second runtime is opened)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.ct = ctypes
+        self.L = ctypes.CDLL(path)
+        self.L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.owned = []
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.L.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        assert rc == 0, "hipEventCreateWithFlags failed (%d)" % rc
+        self.owned.append(ev)
+        return ev
+
+    def record(self, ev, stream_handle):
+        rc = self.L.hipEventRecord(ev, self.ct.c_void_p(stream_handle))
+        assert rc == 0, "hipEventRecord failed (%d)" % rc
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.L.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        assert rc == 0, "hipEventElapsedTime failed (%d)" % rc
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.owned:
+            self.L.hipEventDestroy(ev)
+        self.owned = []
+
+
 def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_parts=0):
     import numpy as np
     import torch
@@ -105,15 +147,17 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
     P = dict(q=q.data_ptr(), kp=kp.data_ptr(), ev=ev.data_ptr(), agn=agn.data_ptr(), sel=sel.data_ptr(),
              ws=ws.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), out=out.data_ptr())
 
+    T = HipTimingEvents() if want_events else None
+
     def step(evs=None):
         if evs is not None:
-            evs[0].record(stream)
+            T.record(evs[0], sh)
         N.nosa_select(shape, P["q"], P["kp"], P["ev"], 0, P["agn"], P["sel"], P["ws"], sh)
         if evs is not None:
-            evs[1].record(stream)
+            T.record(evs[1], sh)
         N.nosa_sparse_decode(shape, P["q"], P["k"], P["v"], w.nbmax, P["sel"], scale, P["out"], P["ws"], sh)
         if evs is not None:
-            evs[2].record(stream)
+            T.record(evs[2], sh)
 
     for _ in range(warmup):
         step()
@@ -127,14 +171,19 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
     res = {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "tokens_per_s": w.batch * steps / wall}
     if want_events:
         # timed region 2: the same steps with HIP events around each kernel launch
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        evs = [[T.create() for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
+        # A bounded spin kernel holds the stream while the host enqueues every step, so the GPU
+        # never waits on the host inside an event pair (Python enqueues three events and two calls
+        # per step, which can take longer than the step itself).
+        torch.cuda._sleep(int(2.4e9 * (steps * 80e-6 + 2e-3)))
         for i in range(steps):
             step(evs[i])
         torch.cuda.synchronize()
-        sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
-        dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-        stp_ms = [e[0].elapsed_time(e[2]) for e in evs]
+        sel_ms = [T.elapsed_ms(e[0], e[1]) for e in evs]
+        dec_ms = [T.elapsed_ms(e[1], e[2]) for e in evs]
+        stp_ms = [T.elapsed_ms(e[0], e[2]) for e in evs]
+        T.close()
         res.update({
             "select_ms_mean": statistics.mean(sel_ms), "decode_ms_mean": statistics.mean(dec_ms),
             "step_ms_median": statistics.median(stp_ms),
@@ -429,14 +478,14 @@ def cpu_baseline(cfg, budget_s=10.0, max_s=30.0):
                       "%.1f s wall, fp64" % (reps, cfg, w.rows, el)}
 
 
-def traffic_record():
+def traffic_record(cfg):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs, if they were taken on
-    the current decode kernel source."""
+    this workload and on the current decode kernel source."""
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     rec = json.load(open(PROFILE_TRAFFIC))
     src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if rec.get("decode_src_sha256") != src_hash:
+    if rec.get("decode_src_sha256") != src_hash or rec.get("workload") != cfg:
         return None
     return rec.get("bytes_per_launch")
 
@@ -511,7 +560,7 @@ def main():
         "roofline": {
             "kernel": "nosa_sparse_decode call: decode_mfma_kernel + combine_kernel (split-K merge)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(),
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(args.config),
             "algorithmic_bytes_per_launch": by["decode"], "avg_launch_ms": main_res["decode_ms_mean"],
         },
         "select_kernel": {"avg_launch_ms": main_res["select_ms_mean"], "algorithmic_bytes": by["select"],
