@@ -38,11 +38,16 @@ _lib: Optional[ctypes.CDLL] = None
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library.  NOSA_ORACLE_LIBRARY names another build of the same source (the
+    mutation test points it at deliberately broken copies to show that the pins catch them)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("NOSA_ORACLE_LIBRARY")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+        L = ctypes.CDLL(path)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.oracle_pool_keys.argtypes = [I64, I64, I, I, P, I, P]
         L.oracle_block_scores.argtypes = [I, I, I, I, I, I, P, I, P, I64, P]

@@ -455,3 +455,34 @@ def test_gather_units_matches_oracle(unit_bytes, pinned_src):
     N.nosa_gather_units(s_t, ns, d_t, nd, unit_bytes, H.dev(su), H.dev(du), 0)   # no-op
     torch.cuda.synchronize()
     assert np.array_equal(H.host(d_t), ref)
+
+
+def test_multistep_select_with_changing_eviction_scores():
+    # Eviction scores redrawn every step: strict eviction on the GPU still admits only previous
+    # members and arrivals, exactly as the oracle (with fixed scores the rule is invisible).
+    w = small_workload("evict_change", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=40,
+                       n_blocks_max=48, kq=5, ke=6, seed=38)
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    kp_dev = H.gpu_pool(shape0, H.dev(x["k"]))
+    ws = N.workspace(shape0)
+    kp_ref = O.pool_keys(x["k"], 32)
+    rng = np.random.default_rng(12)
+    n, agn_dev, agn_ref = 40, None, None
+    s_ref = O.block_scores(x["q"], kp_ref[:, :, :2 * n], n, 2)
+    for t in range(8):
+        n_prev = 0 if t == 0 else n
+        if t in (3, 5):
+            n += 2
+            s_ref = O.block_scores(x["q"], kp_ref[:, :, :2 * n], n, 2)
+        ev = rng.random((w.batch, w.n_kv_heads, w.nbmax), dtype=np.float32)
+        shape = shape0.copy(n_blocks=n)
+        sel, agn_dev = H.gpu_select(shape, H.dev(x["q"]), kp_dev, H.dev(ev), ws, n_prev=n_prev, agn=agn_dev)
+        H.check_selection(H.host(sel), H.host(agn_dev), s_ref, ev, w.kq, w.ke, n_prev, agn_ref)
+        _, agn_ref, _ = O.select(s_ref, ev, w.kq, w.ke, n_prev, agn_ref)
+        if t > 0:
+            # members are previous members or arrivals only
+            prev = set(np.asarray(prev_agn).reshape(-1, w.ke)[0].tolist())
+            cur = set(agn_ref.reshape(-1, w.ke)[0].tolist())
+            assert cur <= prev | set(range(n_prev, n))
+        prev_agn = agn_ref.copy()

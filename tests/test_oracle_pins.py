@@ -530,3 +530,21 @@ def test_gather_units_block_granularity_equals_block_gather():
                 du.append(r * C + ml[b, h, i, 1])
     O.gather_units(host, cache_b, ub, np.array(su), np.array(du))
     assert np.array_equal(cache_a, cache_b)
+
+
+def test_strict_eviction_holds_when_eviction_scores_change():
+    # With scores fixed over time, top-ke of (previous members + arrivals) equals top-ke of all
+    # visible blocks, so only a change of the scores between steps shows the rule itself: a block
+    # outside Gamma_e stays out even when its eviction score rises; arrivals still compete.
+    kw = dict(kq=1, ke=2)
+    e0 = np.array([[[0.9, 0.8, 0.1, 0.2, 0.3, 0.05, 0.0]]], np.float32)
+    sel, st, _ = O.select(np.zeros((1, 1, 6)), e0, **kw)
+    assert st.tolist() == [[[0, 1]]]
+    e1 = np.array([[[0.9, 0.1, 0.95, 0.2, 0.3, 0.05, 0.5]]], np.float32)
+    s1 = np.zeros((1, 1, 6))
+    s1[0, 0, 2] = 7.0
+    sel, st, _ = O.select(s1, e1, n_prev=6, agn_state=st, **kw)
+    assert st.tolist() == [[[0, 1]]]            # block 2 (now 0.95) may not re-enter
+    assert sel.tolist() == [[[0, 1, 2]]]        # but the query-aware part recalls it
+    sel, st, _ = O.select(np.zeros((1, 1, 7)), e1, n_prev=6, agn_state=st, **kw)
+    assert st.tolist() == [[[0, 6]]]            # the arrival (0.5) beats member 1 (now 0.1)
