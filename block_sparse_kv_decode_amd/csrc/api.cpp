@@ -106,9 +106,10 @@ SplitPlan decode_plan(const nosa_shape *s) {
 }
 
 struct PartPlan {
-    int P;         // workgroups scoring one row
-    int bpp;       // blocks per part
-    int threads;   // workgroup size of the one-workgroup-per-row plan (P == 1)
+    int P;              // workgroups scoring one row
+    int bpp;            // blocks per part
+    int threads;        // workgroup size of the one-workgroup-per-row plan (P == 1)
+    int part_threads;   // workgroup size of the multi-part scoring kernel
 };
 
 // Select plan.  Enough rows to fill the chip: one 256-thread workgroup scores and selects a row.
@@ -121,6 +122,7 @@ constexpr size_t kFusedRowBytes = 64 * 1024;
 PartPlan select_plan(const nosa_shape *s) {
     const int R = rows_of(s), n = s->n_blocks;
     const int threads = R >= kTargetWorkgroups / 2 ? 256 : 1024;
+    const int part_threads = n > kLongRowBlocks ? 1024 : 256;
     int P;
     if (s->select_parts > 0) {
         P = s->select_parts;
@@ -129,7 +131,8 @@ PartPlan select_plan(const nosa_shape *s) {
         if (threads == 256 || row_bytes <= kFusedRowBytes) {
             P = 1;
         } else {
-            P = (kTargetWorkgroups + R - 1) / R;
+            const int target = kTargetWorkgroups * 256 / part_threads;
+            P = (target + R - 1) / R;
             const int cap = n / kMinBlocksPerPart > 0 ? n / kMinBlocksPerPart : 1;
             if (P > cap) P = cap;
         }
@@ -138,7 +141,7 @@ PartPlan select_plan(const nosa_shape *s) {
     if (P > n) P = n;
     const int bpp = (n + P - 1) / P;
     P = (n + bpp - 1) / bpp;
-    return {P, bpp, threads};
+    return {P, bpp, threads, part_threads};
 }
 
 struct WsLayout {
@@ -357,7 +360,8 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
     a.blocks_per_part = pp.bpp;
     a.scores_only = scores_only ? 1 : 0;
     a.scores_stride = shape->n_blocks_max;
-    hipError_t e = launch_select(shape->dtype, shape->head_dim, spb_of(shape), a, rows_of(shape), pp.threads, stream);
+    hipError_t e = launch_select(shape->dtype, shape->head_dim, spb_of(shape), a, rows_of(shape), pp.threads,
+                                  pp.part_threads, stream);
     return e == hipSuccess ? ok() : hip_fail(e, scores_only ? "block_scores launch" : "select launch");
 }
 

@@ -67,6 +67,12 @@ struct GatherArgs {
 };
 constexpr int kGatherMaxRows = 8192;   // rows (batch x KV heads) one cache update can serve
 
+// Rows longer than this many blocks are scored by 1024-thread workgroups (the row's Gamma_e
+// workgroup then ranks with four lanes per key); shorter rows by 256-thread workgroups, twice as
+// many per CU.  Measured on MI355X: at 256 blocks per row the 256-thread plan selects in 15.6 us
+// against 17.7 us; at 2048 blocks per row the 1024-thread plan takes 22.7 us against 28.0 us.
+constexpr int kLongRowBlocks = 1024;
+
 struct UnitsArgs {
     const unsigned char *src;       // device address (device memory or mapped pinned host memory)
     unsigned char *dst;
@@ -95,9 +101,10 @@ struct DecodeArgs {
 // Each launcher returns hipSuccess or the error of the launch.
 hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_t st);
 hipError_t launch_append(int dtype, int d, const AppendArgs &a, int rows, hipStream_t st);
-// fused_threads: workgroup size (256 or 1024) of the one-workgroup-per-row plan (parts == 1).
-hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads, hipStream_t st);
-size_t select_lds_bytes(int n_blocks);
+// fused_threads: workgroup size (256 or 1024) of the one-workgroup-per-row plan (parts == 1);
+// part_threads: workgroup size (256 or 1024) of the multi-part scoring kernel.
+hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads, int part_threads,
+                         hipStream_t st);
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t st);
 hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st);

@@ -40,6 +40,7 @@ constexpr int kUnroll = 4;           // groups of eight sub-blocks per wave kept
 constexpr int kRankMaxBlocks = 512;  // rows up to this length use the one-pass rank selection
 constexpr int kCandMax = 512;        // candidates kept after the chunk-maximum bound
 constexpr int kEvPre = 4;            // eviction scores prefetched per thread
+constexpr int kEvLdsMax = 4096;      // rows up to this length keep their eviction scores in LDS
 constexpr int kKeyScratch = 256 + kCandMax;   // uint64 LDS entries of the top-k scratch
 
 template <int NT>
@@ -265,7 +266,7 @@ struct RowLds {
 };
 
 template <int NT>
-__host__ __device__ inline bool ev_in_lds(int n) { return n <= kEvPre * NT; }
+__host__ __device__ inline bool ev_in_lds(int n) { return n <= kEvLdsMax; }
 
 template <int NT>
 __host__ __device__ inline size_t row_lds_bytes(int n) {
@@ -293,7 +294,8 @@ __device__ inline RowLds carve(unsigned char *dyn, int n) {
 }
 
 // Loads up to kEvPre * NT eviction scores of the row into registers (issued early; stored to
-// LDS by ev_store once they are needed).
+// LDS by ev_store once they are needed, together with the rest of a row of up to kEvLdsMax
+// blocks).  Longer rows read their eviction scores from global memory during the top-k.
 template <int NT>
 __device__ __forceinline__ void ev_load(const SelectArgs &a, int row, float (&e)[kEvPre]) {
     const float *evr = a.ev + (size_t)row * a.n_blocks_max;
@@ -305,13 +307,18 @@ __device__ __forceinline__ void ev_load(const SelectArgs &a, int row, float (&e)
 }
 
 template <int NT>
-__device__ __forceinline__ void ev_store(const RowLds &L, int n, const float (&e)[kEvPre]) {
+__device__ __forceinline__ void ev_store(const SelectArgs &a, int row, const RowLds &L, int n,
+                                         const float (&e)[kEvPre]) {
     if (!L.ev) return;
 #pragma unroll
     for (int r = 0; r < kEvPre; ++r) {
         const int i = threadIdx.x + r * NT;
         if (i < n) L.ev[i] = e[r];
     }
+    // the rest of a long row (beyond the prefetch): independent loads, several in flight
+    const float *evr = a.ev + (size_t)row * a.n_blocks_max;
+#pragma unroll 4
+    for (int i = threadIdx.x + kEvPre * NT; i < n; i += NT) L.ev[i] = evr[i];
 }
 
 // Gamma_e of one row into L.inE (all threads of the workgroup): the sink and window blocks plus
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
     float e[kEvPre];
     ev_load<NT>(a, row, e);
     score_range<T, D, SPB, NT>(a, row, 0, a.n_blocks, L.sc, nullptr);
-    ev_store<NT>(L, a.n_blocks, e);
+    ev_store<NT>(a, row, L, a.n_blocks, e);
     __syncthreads();
     select_agnostic<NT>(a, row, L, sh);
     select_query<NT>(a, row, L, sh, true);
@@ -462,25 +469,25 @@ __global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
 // Grid rows x (parts + 1): workgroup `part < parts` scores a slice of the row's blocks into the
 // global score buffer; the extra workgroup `part == parts` (absent in scores-only mode) computes
 // the row's Gamma_e from the eviction scores meanwhile and writes it to agn_state.
-template <typename T, int D, int SPB>
-__global__ __launch_bounds__(256) void score_part_kernel(SelectArgs a) {
+template <typename T, int D, int SPB, int NT>
+__global__ __launch_bounds__(NT) void score_part_kernel(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char dyn[];
-    __shared__ SelectShared<256> sh;
+    __shared__ SelectShared<NT> sh;
     const int nparts = a.parts + (a.scores_only ? 0 : 1);
     const int row = blockIdx.x / nparts, part = blockIdx.x - row * nparts;
     if (part == a.parts) {
-        const RowLds L = carve<256>(dyn, a.n_blocks);
+        const RowLds L = carve<NT>(dyn, a.n_blocks);
         float e[kEvPre];
-        ev_load<256>(a, row, e);
-        ev_store<256>(L, a.n_blocks, e);
-        select_agnostic<256>(a, row, L, sh);
-        compact_outputs<256>(a.n_blocks, L.inE, L.inE, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
-                             nullptr, 0, sh);
+        ev_load<NT>(a, row, e);
+        ev_store<NT>(a, row, L, a.n_blocks, e);
+        select_agnostic<NT>(a, row, L, sh);
+        compact_outputs<NT>(a.n_blocks, L.inE, L.inE, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
+                            nullptr, 0, sh);
         return;
     }
     const int blk_lo = part * a.blocks_per_part;
     const int blk_hi = min(a.n_blocks, blk_lo + a.blocks_per_part);
-    score_range<T, D, SPB, 256>(a, row, blk_lo, blk_hi, nullptr, a.scores + (size_t)row * a.scores_stride);
+    score_range<T, D, SPB, NT>(a, row, blk_lo, blk_hi, nullptr, a.scores + (size_t)row * a.scores_stride);
 }
 
 // Gamma_q of rows scored by score_part_kernel (Gamma_e is already in agn_state): one workgroup per row.
@@ -505,7 +512,6 @@ __global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
     select_query<NT>(a, row, L, sh, false);
 }
 
-size_t select_lds_bytes(int n_blocks) { return row_lds_bytes<1024>(n_blocks); }
 
 template <class K>
 static hipError_t allow_lds(K kern, size_t dyn) {
@@ -514,7 +520,8 @@ static hipError_t allow_lds(K kern, size_t dyn) {
 }
 
 template <typename T, int D, int SPB>
-static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threads, hipStream_t st) {
+static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threads, int part_threads,
+                                  hipStream_t st) {
     hipError_t e;
     if (a.parts == 1 && !a.scores_only) {
         if (fused_threads == 1024) {
@@ -530,10 +537,16 @@ static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threa
         }
         return hipGetLastError();
     }
-    const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<256>(a.n_blocks);
-    if ((e = allow_lds(score_part_kernel<T, D, SPB>, dyn0)) != hipSuccess) return e;
-    score_part_kernel<T, D, SPB>
-        <<<dim3((unsigned)(rows * (a.parts + (a.scores_only ? 0 : 1)))), dim3(256), dyn0, st>>>(a);
+    const unsigned grid = (unsigned)(rows * (a.parts + (a.scores_only ? 0 : 1)));
+    if (part_threads == 1024) {
+        const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<1024>(a.n_blocks);
+        if ((e = allow_lds(score_part_kernel<T, D, SPB, 1024>, dyn0)) != hipSuccess) return e;
+        score_part_kernel<T, D, SPB, 1024><<<dim3(grid), dim3(1024), dyn0, st>>>(a);
+    } else {
+        const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<256>(a.n_blocks);
+        if ((e = allow_lds(score_part_kernel<T, D, SPB, 256>, dyn0)) != hipSuccess) return e;
+        score_part_kernel<T, D, SPB, 256><<<dim3(grid), dim3(256), dyn0, st>>>(a);
+    }
     if ((e = hipGetLastError()) != hipSuccess || a.scores_only) return e;
     // 1024 threads even for short rows: with 256, each thread ranks a whole candidate and the pick
     // takes longer (measured on MI355X at 256 blocks per row: 18.8 vs 17.1 us for the selection).
@@ -544,22 +557,23 @@ static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threa
 }
 
 template <typename T, int D>
-static hipError_t launch_select_d(int spb, const SelectArgs &a, int rows, int fused_threads, hipStream_t st) {
+static hipError_t launch_select_d(int spb, const SelectArgs &a, int rows, int fused_threads, int part_threads,
+                                  hipStream_t st) {
     switch (spb) {
-        case 1: return launch_select_t<T, D, 1>(a, rows, fused_threads, st);
-        case 2: return launch_select_t<T, D, 2>(a, rows, fused_threads, st);
-        case 4: return launch_select_t<T, D, 4>(a, rows, fused_threads, st);
-        default: return launch_select_t<T, D, 8>(a, rows, fused_threads, st);
+        case 1: return launch_select_t<T, D, 1>(a, rows, fused_threads, part_threads, st);
+        case 2: return launch_select_t<T, D, 2>(a, rows, fused_threads, part_threads, st);
+        case 4: return launch_select_t<T, D, 4>(a, rows, fused_threads, part_threads, st);
+        default: return launch_select_t<T, D, 8>(a, rows, fused_threads, part_threads, st);
     }
 }
 
 hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads,
-                         hipStream_t st) {
+                         int part_threads, hipStream_t st) {
     if (dtype == 1)
-        return d == 128 ? launch_select_d<uint16_t, 128>(spb, a, rows, fused_threads, st)
-                        : launch_select_d<uint16_t, 64>(spb, a, rows, fused_threads, st);
-    return d == 128 ? launch_select_d<float, 128>(spb, a, rows, fused_threads, st)
-                    : launch_select_d<float, 64>(spb, a, rows, fused_threads, st);
+        return d == 128 ? launch_select_d<uint16_t, 128>(spb, a, rows, fused_threads, part_threads, st)
+                        : launch_select_d<uint16_t, 64>(spb, a, rows, fused_threads, part_threads, st);
+    return d == 128 ? launch_select_d<float, 128>(spb, a, rows, fused_threads, part_threads, st)
+                    : launch_select_d<float, 64>(spb, a, rows, fused_threads, part_threads, st);
 }
 
 }  // namespace nosa
