@@ -356,6 +356,7 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
     a.n_prev = n_prev;
     a.n_sink = shape->sink_blocks;
     a.n_window = shape->window_blocks;
+    a.rows = rows_of(shape);
     a.parts = pp.P;
     a.blocks_per_part = pp.bpp;
     a.scores_only = scores_only ? 1 : 0;

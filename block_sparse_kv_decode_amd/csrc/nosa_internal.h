@@ -40,6 +40,7 @@ struct SelectArgs {
     int Hq, Hkv, G;
     int n_blocks, n_blocks_max, kq, ke, n_prev;
     int n_sink, n_window;  // blocks always in the query-agnostic subset (start / end of the context)
+    int rows;             // batch x KV heads
     int parts;            // workgroups per row
     int blocks_per_part;
     int scores_only;      // 1: stop after writing block scores

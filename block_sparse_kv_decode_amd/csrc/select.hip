@@ -466,16 +466,21 @@ __global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
     select_query<NT>(a, row, L, sh, true);
 }
 
-// Grid rows x (parts + 1): workgroup `part < parts` scores a slice of the row's blocks into the
-// global score buffer; the extra workgroup `part == parts` (absent in scores-only mode) computes
-// the row's Gamma_e from the eviction scores meanwhile and writes it to agn_state.
+// Grid rows x (parts + 1): one workgroup per row (absent in scores-only mode) computes the row's
+// Gamma_e from the eviction scores and writes it to agn_state, while `parts` workgroups per row
+// score slices of the row's blocks into the global score buffer.
 template <typename T, int D, int SPB, int NT>
 __global__ __launch_bounds__(NT) void score_part_kernel(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ SelectShared<NT> sh;
-    const int nparts = a.parts + (a.scores_only ? 0 : 1);
-    const int row = blockIdx.x / nparts, part = blockIdx.x - row * nparts;
-    if (part == a.parts) {
+    // Workgroups [0, rows) compute Gamma_e (none in scores-only mode); the scoring parts follow.
+    // Dispatched first, the Gamma_e workgroups issue their eviction-score loads before the
+    // scoring parts fill the memory queues with pooled keys.
+    const int n_agn = a.scores_only ? 0 : a.rows;
+    const bool agn_wg = (int)blockIdx.x < n_agn;
+    const int idx = (int)blockIdx.x - n_agn;
+    const int row = agn_wg ? (int)blockIdx.x : idx / a.parts, part = agn_wg ? a.parts : idx - row * a.parts;
+    if (agn_wg) {
         const RowLds L = carve<NT>(dyn, a.n_blocks);
         float e[kEvPre];
         ev_load<NT>(a, row, e);
