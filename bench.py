@@ -28,6 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+LAYERS = 4   # independent buffer sets the resident step rotates over (see run_resident)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_kernel_c2_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_decode_amd", "csrc", "decode.hip")
@@ -111,7 +112,12 @@ class HipTimingEvents:
         self.owned = []
 
 
-def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_parts=0):
+def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_parts=0, layers=LAYERS):
+    """The resident decode step, timed.  Consecutive steps rotate over `layers` independent sets of
+    device buffers (q, K/V stores, pooled keys, eviction scores, outputs), as the attention layers
+    of a model would: one layer's selected K/V (268 MB at bs16 / 16K) is about the size of the
+    GPU's 256 MB last-level cache, and repeating a single layer's step would let that cache serve
+    part of every step.  The sets are copies of one synthetic layer at different addresses."""
     import numpy as np
     import torch
 
@@ -131,46 +137,52 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
                          n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, sub_block_size=32,
                          dtype=N.NOSA_BF16 if w.dtype == "bf16" else N.NOSA_F32, decode_splits=decode_splits,
                          select_parts=select_parts, sink_blocks=w.n_sink, window_blocks=w.n_window)
-    q, k, v, ev = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["evict"])
     R = w.rows
-    kp = torch.empty((R, w.nbmax * 2, w.head_dim), dtype=torch.float32, device="cuda")
-    ws = N.workspace(shape)
-    agn = torch.empty((R, max(w.ke, 1)), dtype=torch.int32, device="cuda")
-    sel = torch.empty((R, w.k), dtype=torch.int32, device="cuda")
-    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device="cuda")
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
-    N.nosa_pool_keys(shape, k, 0, w.nbmax, kp, sh)           # state, off the step timer
+    first = dict(q=dev(x["q"]), k=dev(x["k"]), v=dev(x["v"]), ev=dev(x["evict"]))
+    sets = []
+    for li in range(layers):
+        t = {name: (a if li == 0 else a.clone()) for name, a in first.items()}
+        t["kp"] = torch.empty((R, w.nbmax * 2, w.head_dim), dtype=torch.float32, device="cuda")
+        t["agn"] = torch.empty((R, max(w.ke, 1)), dtype=torch.int32, device="cuda")
+        t["sel"] = torch.empty((R, w.k), dtype=torch.int32, device="cuda")
+        t["out"] = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=t["q"].dtype, device="cuda")
+        N.nosa_pool_keys(shape, t["k"], 0, w.nbmax, t["kp"], sh)           # state, off the step timer
+        sets.append(t)
+    ws = N.workspace(shape)
     torch.cuda.synchronize()
     scale = 1.0 / (w.head_dim ** 0.5)
     # raw pointers, resolved once: the timed loop only enqueues
-    P = dict(q=q.data_ptr(), kp=kp.data_ptr(), ev=ev.data_ptr(), agn=agn.data_ptr(), sel=sel.data_ptr(),
-             ws=ws.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), out=out.data_ptr())
+    P = [{name: a.data_ptr() for name, a in t.items()} for t in sets]
+    wsp = ws.data_ptr()
 
     T = HipTimingEvents() if want_events else None
 
-    def step(evs=None):
+    def step(i, evs=None):
+        p = P[i % layers]
         if evs is not None:
             T.record(evs[0], sh)
-        N.nosa_select(shape, P["q"], P["kp"], P["ev"], 0, P["agn"], P["sel"], P["ws"], sh)
+        N.nosa_select(shape, p["q"], p["kp"], p["ev"], 0, p["agn"], p["sel"], wsp, sh)
         if evs is not None:
             T.record(evs[1], sh)
-        N.nosa_sparse_decode(shape, P["q"], P["k"], P["v"], w.nbmax, P["sel"], scale, P["out"], P["ws"], sh)
+        N.nosa_sparse_decode(shape, p["q"], p["k"], p["v"], w.nbmax, p["sel"], scale, p["out"], wsp, sh)
         if evs is not None:
             T.record(evs[2], sh)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     # timed region 1: the plain step loop (headline value)
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    res = {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "tokens_per_s": w.batch * steps / wall}
+    res = {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "tokens_per_s": w.batch * steps / wall,
+           "layers": layers}
     if want_events:
-        # timed region 2: the same steps with HIP events around each kernel launch
+        # timed region 2: the same steps with HIP events around each call
         evs = [[T.create() for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
         # A bounded spin kernel holds the stream while the host enqueues every step, so the GPU
@@ -178,7 +190,7 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
         # per step, which can take longer than the step itself).
         torch.cuda._sleep(int(2.4e9 * (steps * 80e-6 + 2e-3)))
         for i in range(steps):
-            step(evs[i])
+            step(i, evs[i])
         torch.cuda.synchronize()
         sel_ms = [T.elapsed_ms(e[0], e[1]) for e in evs]
         dec_ms = [T.elapsed_ms(e[1], e[2]) for e in evs]
@@ -551,7 +563,8 @@ def main():
         "data": "synthetic (seeded PCG64; K with per-block mean offsets, V ~N(0,1), eviction scores ~U(0,1))",
         "config": {"workload": describe(w), "batch": w.batch, "context": w.n_tokens, "block": 64,
                    "budget_blocks": w.k, "kq": w.kq, "ke": w.ke, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
-                   "head_dim": w.head_dim, "layers": 1, "step": "nosa_select + nosa_sparse_decode"},
+                   "head_dim": w.head_dim, "layers": 1, "step": "nosa_select + nosa_sparse_decode",
+                   "buffer_sets_rotated": main_res["layers"]},
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": by["step"],

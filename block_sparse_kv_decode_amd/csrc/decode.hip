@@ -453,9 +453,8 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
 #pragma unroll 4
     for (int s = 0; s < a.St; ++s) {
         const float *ps = rp + s * stride;
-        const float ms = ps[0];
+        const float ms = ps[0], ls = ps[1], as = ps[2 + dd];   // loaded together, tested after
         if (ms == -INFINITY) continue;
-        const float ls = ps[1], as = ps[2 + dd];
         const float mn = fmaxf(M, ms);
         const float fo = fast_exp2(M - mn), fn = fast_exp2(ms - mn);
         L = L * fo + ls * fn;
