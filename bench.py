@@ -56,7 +56,8 @@ def inputs(cfg):
 
 
 def algorithmic_bytes(w):
-    """Bytes the method must move per step (measurement section)."""
+    """Bytes the method must move per step: the selected K and V blocks, the fp32 pooled keys and
+    the eviction scores of every visible block, q, the output, and the selected ids."""
     eb = 2 if w.dtype == "bf16" else 4
     R, k, d, B, Hq = w.rows, w.k, w.head_dim, w.batch, w.n_q_heads
     kv_sel = R * k * 64 * d * eb * 2                      # selected K and V blocks
@@ -524,8 +525,8 @@ def main():
                     help="only run a plain elementwise copy of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (rows shard across GPUs "
-              "with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (rows would shard "
+              "across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
