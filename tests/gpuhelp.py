@@ -83,13 +83,17 @@ def check_attention(out_gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str 
     g = as_f64(out_gpu) if out_gpu.dtype == np.uint16 else out_gpu.astype(np.float64)
     assert np.all(np.isfinite(g)), "%s: non-finite GPU output" % what
     err = np.abs(g - ref)
+    # normwise error of every output row (one query head of one sequence), reported
+    d = ref.shape[-1]
+    norm_rel = np.linalg.norm((g - ref).reshape(-1, d), axis=1) / np.maximum(
+        np.linalg.norm(ref.reshape(-1, d), axis=1), 1e-30)
     if dtype == "bf16":
         rel = err / np.maximum(np.abs(ref), BF16_FLOOR)
-        stats = {"max_rel": float(rel.max()), "mean_abs": float(err.mean())}
+        stats = {"max_rel": float(rel.max()), "mean_abs": float(err.mean()), "max_row_normwise": float(norm_rel.max())}
         assert rel.max() <= BF16_REL, "%s: max relative error %.3g > %g" % (what, rel.max(), BF16_REL)
         assert err.mean() <= BF16_MEAN_ABS, "%s: mean abs error %.3g > %g" % (what, err.mean(), BF16_MEAN_ABS)
     else:
-        stats = {"max_abs": float(err.max())}
+        stats = {"max_abs": float(err.max()), "max_row_normwise": float(norm_rel.max())}
         assert err.max() <= F32_ABS, "%s: max abs error %.3g > %g" % (what, err.max(), F32_ABS)
     return stats
 
