@@ -486,3 +486,21 @@ def test_multistep_select_with_changing_eviction_scores():
             cur = set(agn_ref.reshape(-1, w.ke)[0].tolist())
             assert cur <= prev | set(range(n_prev, n))
         prev_agn = agn_ref.copy()
+
+
+@pytest.mark.parametrize("k,splits,G,d", [(600, 0, 8, 128), (600, 37, 4, 128), (257, 0, 1, 64), (1000, 0, 2, 64)])
+def test_sparse_decode_large_budget(k, splits, G, d):
+    # Budgets of hundreds of blocks (tens of thousands of tokens): many splits, a merge over many
+    # partials, ragged last splits (600 = 37 * 16 + 8), and the automatic plan.
+    n = k + 40
+    w = small_workload("large_k", batch=1, n_q_heads=2 * G, n_kv_heads=2, head_dim=d, n_blocks=n, kq=k // 2,
+                       ke=k - k // 2, seed=40 + k % 7)
+    x = generate(w)
+    shape = H.shape_of(w, decode_splits=splits)
+    rng = np.random.default_rng(k)
+    table = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(w.rows)]).astype(np.int32)
+    table = table.reshape(w.batch, w.n_kv_heads, k)
+    out = H.gpu_decode(shape, H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), w.nbmax, H.dev(table), N.workspace(shape))
+    torch.cuda.synchronize()
+    ref = O.attention(x["q"], x["k"], x["v"], table)
+    print(H.check_attention(H.host(out), ref, w.dtype, "k=%d" % k))
