@@ -9,8 +9,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "nosa_internal.h"
 
 using namespace nosa;
@@ -41,6 +39,8 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Rows (batch x KV heads) per call: keeps every grid (rows x splits or parts) within 2^31 workgroups.
+constexpr int kMaxRows = 1 << 16;
 // Work distribution targets: enough workgroups to give every one of the 256 CUs two of them.
 constexpr int kTargetWorkgroups = 512;
 constexpr int kMinBlocksPerPart = 8;
@@ -52,6 +52,9 @@ int check_shape(const nosa_shape *s) {
     if (!s) return fail(NOSA_EINVAL, "shape is NULL");
     if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
         return fail(NOSA_EINVAL, "batch, n_q_heads and n_kv_heads must be >= 1");
+    if ((long long)s->batch * s->n_kv_heads > kMaxRows)
+        return fail(NOSA_EUNSUPPORTED, "batch x n_kv_heads = %lld exceeds %d", (long long)s->batch * s->n_kv_heads,
+                    kMaxRows);
     if (s->n_q_heads % s->n_kv_heads != 0)
         return fail(NOSA_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", s->n_q_heads, s->n_kv_heads);
     const int G = s->n_q_heads / s->n_kv_heads;
@@ -173,21 +176,20 @@ WsLayout ws_layout(const nosa_shape *s) {
         if (!aligned((p), (al))) return fail(NOSA_EINVAL, "%s is not %d-byte aligned", #p, (int)(al)); \
     } while (0)
 
-// Two events per device order the copy stream after the map update and the compute stream after
-// the transfer.  Created on first use and kept for the life of the process.
+// Two events per (host thread, device) order the copy stream after the map update and the compute
+// stream after the transfer.  Per thread, so that calls made from different host threads never wait
+// on each other's events; created on first use and kept for the life of the thread.
 struct DeviceEvents {
     hipEvent_t mapped = nullptr, copied = nullptr;
 };
 constexpr int kMaxDevices = 64;
-DeviceEvents g_events[kMaxDevices];
-std::mutex g_events_mu;
+thread_local DeviceEvents g_events[kMaxDevices];
 
 int get_events(DeviceEvents **out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices) return fail(NOSA_EUNSUPPORTED, "device index %d too large", dev);
-    std::lock_guard<std::mutex> lock(g_events_mu);
     DeviceEvents &d = g_events[dev];
     if (!d.mapped) {
         if ((e = hipEventCreateWithFlags(&d.mapped, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");

@@ -30,10 +30,11 @@
  *     r = b * n_kv_heads + g, and query head h belongs to KV head h / (n_q_heads / n_kv_heads).
  *   - Element type of q, K, V and the output: NOSA_BF16 (bfloat16) or NOSA_F32.  Pooled keys,
  *     eviction scores and block scores are float32.  Accumulation is float32 everywhere.
- *   - Supported set: head_dim 64 or 128; block_size 64; sub_block_size 8, 16, 32 or 64;
- *     n_q_heads / n_kv_heads in {1, 2, 4, 8}; 1 <= kq + ke <= n_blocks <= n_blocks_max <= 16384;
- *     cache_slots >= kq + ke (for nosa_cache_update and nosa_offload_decode).  Anything else returns NOSA_EUNSUPPORTED
- *     or NOSA_EINVAL.
+ *   - Supported set: batch x n_kv_heads <= 65536; head_dim 64 or 128; block_size 64;
+ *     sub_block_size 8, 16, 32 or 64; n_q_heads / n_kv_heads in {1, 2, 4, 8};
+ *     1 <= kq + ke <= n_blocks <= n_blocks_max <= 16384; cache_slots >= kq + ke (for
+ *     nosa_cache_update and nosa_offload_decode).  Anything else returns NOSA_EUNSUPPORTED or
+ *     NOSA_EINVAL.
  *   - Workspace: nosa_workspace_bytes() bytes of device memory, 256-byte aligned, no initial
  *     contents required (it holds block scores and split-K partials between the kernels of one
  *     call).  Calls that share a workspace must be ordered (same stream, or synchronised);
@@ -192,7 +193,8 @@ int nosa_select(const nosa_shape *shape, const void *q, const float *pooled_k, c
  *   cache_k/cache_v : device, [B, Hkv, C, block_size, d], dtype; missed blocks are copied in
  *   compute       : stream of the map update; copy : stream of the block transfer (may equal
  *                   compute or be NULL = compute).  On return, work later enqueued on `compute`
- *                   is ordered after the transfer.
+ *                   is ordered after the transfer.  A distinct copy stream is ordered through two
+ *                   HIP events that the library creates once per host thread and device.
  * Selected ids outside [0, n_blocks_max) are skipped.  Maps that are not mutual inverses are
  * outside the contract.
  */

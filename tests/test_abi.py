@@ -172,3 +172,9 @@ def test_gather_units_rejects_on_host():
     with pytest.raises(N.NosaError):
         N.nosa_gather_units(16, 4, 8, 4, 256, 16, 16, 1, stream=0)        # dst misaligned
     N.nosa_gather_units(None, 0, None, 0, 256, None, None, 0, stream=0)   # zero units: no-op
+
+
+def test_rows_limit_rejected_on_host():
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_select(_good(batch=10000, n_kv_heads=8, n_q_heads=32), 16, 16, 16, 0, 16, 16, 256, stream=0)
+    assert ei.value.code == N.NOSA_EUNSUPPORTED

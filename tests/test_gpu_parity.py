@@ -504,3 +504,65 @@ def test_sparse_decode_large_budget(k, splits, G, d):
     torch.cuda.synchronize()
     ref = O.attention(x["q"], x["k"], x["v"], table)
     print(H.check_attention(H.host(out), ref, w.dtype, "k=%d" % k))
+
+
+def test_offload_decode_from_two_host_threads():
+    # Two host threads drive independent offload loops, each with its own compute and copy streams:
+    # every step's maps, table, cache bytes and output are bit-identical to the same loop run alone.
+    import threading
+    w = small_workload("threads", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=40, n_blocks_max=44,
+                       kq=6, ke=6, seed=39, cache_slots=12)
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    R, k, C = w.rows, w.k, w.cache_slots
+    hk, hv = H.pinned(x["k"]), H.pinned(x["v"])
+    kp_dev = H.gpu_pool(shape0, H.dev(x["k"]))
+    ev_dev = H.dev(x["evict"])
+    rng = np.random.default_rng(10)
+    from nosa_inputs import f32_to_bf16_bits
+    qs = [x["q"]]
+    for _ in range(7):
+        qs.append(f32_to_bf16_bits((H.as_f64(qs[-1]) + 0.4 * rng.standard_normal(x["q"].shape)).astype(np.float32)))
+    q_dev = [H.dev(q) for q in qs]
+    torch.cuda.synchronize()
+
+    def run(results, key):
+        torch.cuda.set_device(0)
+        compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+        with torch.cuda.stream(compute):
+            ck = torch.zeros((w.batch, w.n_kv_heads, C, 64, 128), dtype=torch.bfloat16, device="cuda")
+            cv = torch.zeros_like(ck)
+            sob = torch.full((R, w.nbmax), -1, dtype=torch.int32, device="cuda")
+            bos = torch.full((R, C), -1, dtype=torch.int32, device="cuda")
+            table = torch.zeros((R, k), dtype=torch.int32, device="cuda")
+            mcnt = torch.zeros((R,), dtype=torch.int32, device="cuda")
+            mlist = torch.zeros((R, k, 2), dtype=torch.int32, device="cuda")
+            agn = torch.zeros((R, w.ke), dtype=torch.int32, device="cuda")
+            sel = torch.zeros((R, k), dtype=torch.int32, device="cuda")
+            ws = N.workspace(shape0)
+            rec = []
+            for t in range(8):
+                out = torch.zeros((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+                N.nosa_select(shape0, q_dev[t], kp_dev, ev_dev, 0 if t == 0 else w.n_blocks, agn, sel, ws, compute)
+                N.nosa_offload_decode(shape0, q_dev[t], sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv,
+                                      1.0 / np.sqrt(128), out, ws, compute, copy)
+                rec.append((out, table.clone(), mcnt.clone(), sob.clone()))
+            rec.append((ck, cv))
+        compute.synchronize()
+        results[key] = rec
+
+    alone = {}
+    run(alone, "a")
+    both = {}
+    th = [threading.Thread(target=run, args=(both, i)) for i in range(2)]
+    for t_ in th:
+        t_.start()
+    for t_ in th:
+        t_.join()
+    torch.cuda.synchronize()
+    for i in range(2):
+        for step_a, step_b in zip(alone["a"], both[i]):
+            for a_, b_ in zip(step_a, step_b):
+                if a_.dtype == torch.bfloat16:
+                    a_, b_ = a_.view(torch.int16), b_.view(torch.int16)
+                assert torch.equal(a_, b_), "thread %d differs from the loop run alone" % i
