@@ -1,9 +1,10 @@
 """Benchmark of the NOSA decode-step hot path on one MI355X.
 
 A step is one decode step of one attention layer for every sequence of the batch, GPU-resident:
-nosa_select (pooled-key block scoring + query-agnostic / query-aware selection) followed by
-nosa_sparse_decode (split-K GQA attention over the selected blocks).  Pooled keys are state
-built once before timing (they change only when a block fills up).  tokens/s = batch / step time.
+nosa_decode_step, which is nosa_select (pooled-key block scoring + query-agnostic / query-aware
+selection) followed by nosa_sparse_decode (split-K GQA attention over the selected blocks) in one
+call.  Pooled keys are state built once before timing (they change only when a block fills up).
+tokens/s = batch / step time.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--config C2] [--also C3,F1]
                   [--no-cpu-baseline] [--no-offload] [--no-transfer]
@@ -160,7 +161,14 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
 
     T = HipTimingEvents() if want_events else None
 
-    def step(i, evs=None):
+    def step(i):
+        """The product's decode step: one nosa_decode_step call."""
+        p = P[i % layers]
+        N.nosa_decode_step(shape, p["q"], p["kp"], p["ev"], 0, p["agn"], p["sel"], p["k"], p["v"], w.nbmax, scale,
+                           p["out"], wsp, sh)
+
+    def two_calls(i, evs=None):
+        """The same step as nosa_select + nosa_sparse_decode, with events between the two calls."""
         p = P[i % layers]
         if evs is not None:
             T.record(evs[0], sh)
@@ -171,31 +179,46 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
         if evs is not None:
             T.record(evs[2], sh)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region 1: the plain step loop (headline value)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    res = {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "tokens_per_s": w.batch * steps / wall,
-           "layers": layers}
-    if want_events:
-        # timed region 2: the same steps with HIP events around each call
-        evs = [[T.create() for _ in range(3)] for _ in range(steps)]
+    def wall(fn):
+        for i in range(warmup):
+            fn(i)
         torch.cuda.synchronize()
-        # A bounded spin kernel holds the stream while the host enqueues every step, so the GPU
-        # never waits on the host inside an event pair (Python enqueues three events and two calls
-        # per step, which can take longer than the step itself).
-        torch.cuda._sleep(int(2.4e9 * (steps * 80e-6 + 2e-3)))
+        t0 = time.perf_counter()
         for i in range(steps):
-            step(i, evs[i])
+            fn(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    # timed region 1: the plain step loop (headline value)
+    wall_s = wall(step)
+    res = {"wall_s": wall_s, "ms_per_step": 1e3 * wall_s / steps, "tokens_per_s": w.batch * steps / wall_s,
+           "layers": layers, "ms_per_step_two_calls": 1e3 * wall(two_calls) / steps}
+    if want_events:
+        # A bounded spin kernel holds the stream while the host enqueues the event-timed steps, so
+        # the GPU never waits on the host inside an event pair (Python can take longer to enqueue a
+        # step than the GPU takes to run it).
+        def hold():
+            torch.cuda.synchronize()
+            torch.cuda._sleep(int(2.4e9 * (steps * 80e-6 + 2e-3)))
+
+        # timed region 2: the two-call step with events around each call (the attention call is
+        # the step's dominant kernel: the roofline figure)
+        evs = [[T.create() for _ in range(3)] for _ in range(steps)]
+        hold()
+        for i in range(steps):
+            two_calls(i, evs[i])
         torch.cuda.synchronize()
         sel_ms = [T.elapsed_ms(e[0], e[1]) for e in evs]
         dec_ms = [T.elapsed_ms(e[1], e[2]) for e in evs]
-        stp_ms = [T.elapsed_ms(e[0], e[2]) for e in evs]
+        # timed region 3: events around every nosa_decode_step call
+        evs1 = [[T.create() for _ in range(2)] for _ in range(steps)]
+        hold()
+        for i in range(steps):
+            T.record(evs1[i][0], sh)
+            step(i)
+            T.record(evs1[i][1], sh)
+        torch.cuda.synchronize()
+        stp_ms = [T.elapsed_ms(e[0], e[1]) for e in evs1]
         T.close()
         res.update({
             "select_ms_mean": statistics.mean(sel_ms), "decode_ms_mean": statistics.mean(dec_ms),
@@ -575,11 +598,13 @@ def main():
         "data": "synthetic (seeded PCG64; K with per-block mean offsets, V ~N(0,1), eviction scores ~U(0,1))",
         "config": {"workload": describe(w), "batch": w.batch, "context": w.n_tokens, "block": 64,
                    "budget_blocks": w.k, "kq": w.kq, "ke": w.ke, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
-                   "head_dim": w.head_dim, "layers": 1, "step": "nosa_select + nosa_sparse_decode",
+                   "head_dim": w.head_dim, "layers": 1,
+                   "step": "nosa_decode_step: selection + attention in one call",
                    "buffer_sets_rotated": main_res["layers"]},
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": by["step"],
+        "ms_per_step_two_calls": main_res["ms_per_step_two_calls"],
         "step_ms_median_events": main_res["step_ms_median"],
         "step_ms_p10_p90_events": [main_res["step_ms_p10"], main_res["step_ms_p90"]],
         "roofline": {
@@ -597,6 +622,7 @@ def main():
         b2 = r["bytes"]
         also[cfg] = {
             "workload": describe(r["workload"]), "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+            "ms_per_step_two_calls": r["ms_per_step_two_calls"],
             "step_hbm_gbps": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
             "step_hbm_frac": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "decode_gbps": b2["decode"] / (r["decode_ms_mean"] * 1e-3) / 1e9,

@@ -8,6 +8,6 @@ from .binding import (  # noqa: F401
     EXPORTED, LIB_PATH, NOSA_BF16, NOSA_EHIP, NOSA_EINVAL, NOSA_ECAPACITY, NOSA_EUNSUPPORTED, NOSA_F32,
     NOSA_OK, NosaError, NosaShape, lib, make_shape, nosa_block_scores, nosa_cache_update,
     nosa_last_error, nosa_pool_keys, nosa_append_kv, nosa_select, nosa_sparse_decode, nosa_version,
-    nosa_offload_decode, nosa_gather_units,
+    nosa_offload_decode, nosa_gather_units, nosa_decode_step,
     nosa_workspace_bytes, workspace,
 )

@@ -28,7 +28,7 @@ NOSA_F32, NOSA_BF16 = 0, 1
 EXPORTED = (
     "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
     "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode", "nosa_offload_decode",
-    "nosa_gather_units",
+    "nosa_gather_units", "nosa_decode_step",
 )
 
 
@@ -91,6 +91,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_select.argtypes = [SP, P, P, P, I32, P, P, P, P]
     L.nosa_cache_update.restype = ctypes.c_int
     L.nosa_cache_update.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P]
+    L.nosa_decode_step.restype = ctypes.c_int
+    L.nosa_decode_step.argtypes = [SP, P, P, P, I32, P, P, P, P, I32, ctypes.c_float, P, P, P]
     L.nosa_gather_units.restype = ctypes.c_int
     L.nosa_gather_units.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int64, P]
     L.nosa_offload_decode.restype = ctypes.c_int
@@ -196,3 +198,10 @@ def nosa_gather_units(src, src_units, dst, dst_units, unit_bytes, src_unit, dst_
                       stream=None) -> None:
     _check(lib.nosa_gather_units(_p(src), int(src_units), _p(dst), int(dst_units), int(unit_bytes), _p(src_unit),
                                  _p(dst_unit), int(n_units), _stream(stream)))
+
+
+def nosa_decode_step(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, k_store, v_store, store_blocks,
+                     softmax_scale, out, ws, stream=None) -> None:
+    _check(lib.nosa_decode_step(ctypes.byref(shape), _p(q), _p(pooled_k), _p(evict), int(n_blocks_prev),
+                                _p(agn_state), _p(selected), _p(k_store), _p(v_store), int(store_blocks),
+                                ctypes.c_float(softmax_scale), _p(out), _p(ws), _stream(stream)))

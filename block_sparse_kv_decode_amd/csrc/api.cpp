@@ -47,6 +47,10 @@ constexpr int kMinBlocksPerPart = 8;
 // A split shorter than this many blocks spends more time filling its load pipeline and merging
 // than it saves (measured on MI355X: 4-block splits lose to 8-block splits at 128K context).
 constexpr int kMinBlocksPerSplit = 8;
+// Rows up to this many blocks run the fused decode step: their Gamma_q ranking in a 256-thread
+// workgroup is a single pass.  Longer rows rank more slowly there than the attention splits can
+// hide (measured on MI355X at 2048 blocks per row: 48.7 us per step fused vs 44.2 us in two calls).
+constexpr int kStepMaxBlocks = 512;
 
 int check_shape(const nosa_shape *s) {
     if (!s) return fail(NOSA_EINVAL, "shape is NULL");
@@ -161,9 +165,10 @@ WsLayout ws_layout(const nosa_shape *s) {
     // With a cache configured, nosa_offload_decode fills 2 S partial slots per row (hits, then
     // misses) and keeps the hit-only table beside them.
     const bool offload = s->cache_slots >= s->kq + s->ke;
+    // The fused decode step uses up to S + 1 (Gamma_e and Gamma_q splits are rounded up apart).
+    const size_t slots = offload ? (size_t)(2 * dp.S > dp.S + 1 ? 2 * dp.S : dp.S + 1) : (size_t)dp.S + 1;
     L.part = off;
-    off = round_up(off + R * (size_t)(offload ? 2 : 1) * dp.S * group_of(s) * (size_t)(s->head_dim + 2) * sizeof(float),
-                   kAlign);
+    off = round_up(off + R * slots * group_of(s) * (size_t)(s->head_dim + 2) * sizeof(float), kAlign);
     L.tab_hit = off;
     if (offload) off = round_up(off + R * (size_t)(s->kq + s->ke) * sizeof(int32_t), kAlign);
     L.total = off;
@@ -321,9 +326,11 @@ int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst
     return e == hipSuccess ? ok() : hip_fail(e, "gather_units launch");
 }
 
+// The selection launch(es).  no_pick: the multi-part plan stops after scoring and Gamma_e (the
+// fused decode step ranks Gamma_q); *used receives the launch descriptor when not NULL.
 static int run_scores(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
                       int32_t n_prev, int32_t *agn_state, int32_t *selected, float *scores_out, void *ws,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool no_pick = false, SelectArgs *used = nullptr) {
     const bool scores_only = scores_out != nullptr;
     REQUIRE_PTR(q, 16);
     REQUIRE_PTR(pooled_k, 16);
@@ -362,7 +369,9 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
     a.parts = pp.P;
     a.blocks_per_part = pp.bpp;
     a.scores_only = scores_only ? 1 : 0;
+    a.no_pick = no_pick ? 1 : 0;
     a.scores_stride = shape->n_blocks_max;
+    if (used) *used = a;
     hipError_t e = launch_select(shape->dtype, shape->head_dim, spb_of(shape), a, rows_of(shape), pp.threads,
                                   pp.part_threads, stream);
     return e == hipSuccess ? ok() : hip_fail(e, scores_only ? "block_scores launch" : "select launch");
@@ -550,6 +559,42 @@ int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *s
     a.s0 = a.S;
     e = launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, true);
     return e == hipSuccess ? ok() : hip_fail(e, "offload_decode miss launch");
+}
+
+int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                     int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, const void *k_store,
+                     const void *v_store, int32_t store_blocks, float softmax_scale, void *out, void *ws,
+                     hipStream_t stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_decode_args(q, k_store, v_store, store_blocks, softmax_scale, out, ws)) != NOSA_OK) return rc;
+    const PartPlan pp = select_plan(shape);
+    const SplitPlan dp = decode_plan(shape);
+    // The pick moves into the attention launch when the selection would otherwise need its own
+    // Gamma_q kernel (multi-part plan), for bf16 rows with both subsets non-empty.
+    const bool fused = shape->dtype == NOSA_BF16 && pp.P > 1 && shape->kq > 0 && shape->ke > 0 &&
+                       shape->n_blocks <= kStepMaxBlocks;
+    if (!fused) {
+        if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream)))
+            return rc;
+        DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
+        a.table = selected;
+        hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream, true);
+        return e == hipSuccess ? ok() : hip_fail(e, "decode_step attention launch");
+    }
+    SelectArgs sa;
+    if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream, true,
+                         &sa)))
+        return rc;
+    DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
+    const int S_e = (shape->ke + dp.nbs - 1) / dp.nbs, S_q = (shape->kq + dp.nbs - 1) / dp.nbs;
+    a.table = nullptr;
+    a.S = S_e + S_q;
+    a.St = S_e + S_q;
+    a.s0 = 0;
+    a.direct = 0;
+    hipError_t e = launch_step_decode(shape->head_dim, group_of(shape), a, sa, rows_of(shape), S_e, S_q, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "decode_step launch");
 }
 
 int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store, const void *v_store,

@@ -33,6 +33,7 @@
 // merges both.
 #include "nosa_device.h"
 #include "nosa_internal.h"
+#include "select_core.h"
 
 namespace nosa {
 
@@ -171,21 +172,20 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, int row, int s
 }  // namespace
 
 // ---- bf16: QK on the matrix cores -----------------------------------------------------------
+// One split: entries [j0, j1) of the row's table (tab[j * tab_stride], block ids into the store),
+// written as partial slot sp of the row (or the output itself when a.direct).
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_mfma_split(const DecodeArgs &a, int row, int sp, const int32_t *tab,
+                                                  int tab_stride, int j0, int j1, SplitShared<D, G> &sh) {
     using Gm = Geom<uint16_t, D>;
     constexpr int KS = D / 32;                        // 32-dim MFMA steps
     constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB, TPI = Gm::TPI;
     static_assert(CPL == KS, "bf16 rows: one V chunk per MFMA step");
-    __shared__ SplitShared<D, G> sh;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int j16 = lane & 15, grp = lane >> 4;       // MFMA layout: column (head) / k-group
     const int cpv = lane % NC, tpv = lane / NC;       // PV layout
-    const int n_use = a.count ? min(a.k_sel, a.count[row]) : a.k_sel;
-    const int j0 = sp * a.nbs, j1 = min(n_use, j0 + a.nbs);
 
     // B operand: q of head j16 (zero columns beyond G), dims 32 ks + 8 grp .. + 8
     bf16x8_t qb[KS];
@@ -265,9 +265,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         wave_lds_sync();
     };
 
-    const int32_t *tab = a.table + (size_t)row * a.k_sel * a.tab_stride;
     auto load = [&](int j, uint4(&kk)[KS], uint4(&vv)[CPL]) -> bool {
-        const int blk = tab[(size_t)j * a.tab_stride];
+        const int blk = tab[(size_t)j * tab_stride];
         if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
         const char *kp = kbase + (size_t)blk * blk_bytes;
         const char *vp = vbase + (size_t)blk * blk_bytes;
@@ -307,6 +306,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         l_h[h] = readlane_f(lt, h);
     }
     finish_split<uint16_t, D, G>(a, row, sp, m_h, l_h, acc, sh);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+    __shared__ SplitShared<D, G> sh;
+    const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
+    const int n_use = a.count ? min(a.k_sel, a.count[row]) : a.k_sel;
+    const int j0 = sp * a.nbs, j1 = min(n_use, j0 + a.nbs);
+    decode_mfma_split<D, G>(a, row, sp, a.table + (size_t)row * a.k_sel * a.tab_stride, a.tab_stride, j0, j1, sh);
 }
 
 // ---- fp32: QK on the VALU ------------------------------------------------------------------
@@ -440,6 +448,50 @@ __global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_k
     finish_split<float, D, G>(a, row, sp, m_h, l_h, acc, sh);
 }
 
+// ---- the decode step with the query-aware pick inside the attention launch -------------------
+// Grid rows x (S_e + S_q), bf16.  Once the scoring kernel has written the block scores and
+// Gamma_e (agn_state), a row's S_e first splits attend the Gamma_e blocks straight away, while each
+// of its S_q last splits ranks the row's Gamma_q in LDS (the first of them also writes the row's
+// selection, the ascending union) and then attends its slice of Gamma_q.  Attention does not
+// depend on the order of the blocks, so the pick hides under the Gamma_e splits' streaming instead
+// of taking a kernel of its own.  Every split writes partial slot sp; combine_kernel merges them.
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, SelectArgs s, int S_e, int S_q) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ SplitShared<D, G> sh;
+    __shared__ SelectShared<256> ssh;
+    const int St = S_e + S_q;
+    const int row = blockIdx.x / St, sp = blockIdx.x - row * St;
+    if (sp < S_e) {
+        const int j0 = sp * a.nbs, j1 = min(s.ke, j0 + a.nbs);
+        decode_mfma_split<D, G>(a, row, sp, s.agn + (size_t)row * s.ke, 1, j0, j1, sh);
+        return;
+    }
+    const int n = s.n_blocks, tid = threadIdx.x;
+    const RowLds L = carve<256>(dyn, n);
+    int32_t *qlist = (int32_t *)(dyn + row_lds_bytes<256>(n));   // [kq] Gamma_q, ascending
+    const float *gscore = s.scores + (size_t)row * s.scores_stride;
+    for (int i = tid; i < n; i += 256) {
+        L.sc[i] = gscore[i];
+        L.inE[i] = 0;
+        L.inQ[i] = 0;
+    }
+    __syncthreads();
+    for (int j = tid; j < s.ke; j += 256) {
+        const int id = s.agn[(size_t)row * s.ke + j];
+        if (id >= 0 && id < n) L.inE[id] = 1;
+    }
+    __syncthreads();
+    topk_mark<256>(
+        n, s.kq, [&](int i) { return order_key(L.sc[i]); }, [&](int i) { return !L.inE[i]; }, L.inQ, L.keys, ssh);
+    const int k = s.kq + s.ke;
+    if (sp == S_e) compact_outputs<256>(n, L.inE, L.inQ, nullptr, 0, s.sel + (size_t)row * k, k, ssh);
+    compact_outputs<256>(n, L.inQ, L.inQ, qlist, s.kq, nullptr, 0, ssh);
+    __syncthreads();
+    const int j0 = (sp - S_e) * a.nbs, j1 = min(s.kq, j0 + a.nbs);
+    decode_mfma_split<D, G>(a, row, sp, qlist, 1, j0, j1, sh);
+}
+
 // Merges the St split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
 // Empty partials (max = -inf) carry nothing and are passed over.
 template <typename T, int D, int G>
@@ -484,6 +536,38 @@ static hipError_t launch_decode_d(int G, const DecodeArgs &a, int rows, hipStrea
         case 4: return launch_decode_t<T, D, 4>(a, rows, st, merge);
         default: return launch_decode_t<T, D, 8>(a, rows, st, merge);
     }
+}
+
+template <int D, int G>
+static hipError_t launch_step_t(const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
+                                hipStream_t st) {
+    const size_t dyn = row_lds_bytes<256>(s.n_blocks) + 4 * (size_t)s.kq;
+    if (dyn > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)step_decode_kernel<D, G>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    step_decode_kernel<D, G><<<dim3((unsigned)(rows * (S_e + S_q))), dim3(256), dyn, st>>>(a, s, S_e, S_q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    combine_kernel<uint16_t, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_step_d(int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
+                                hipStream_t st) {
+    switch (G) {
+        case 1: return launch_step_t<D, 1>(a, s, rows, S_e, S_q, st);
+        case 2: return launch_step_t<D, 2>(a, s, rows, S_e, S_q, st);
+        case 4: return launch_step_t<D, 4>(a, s, rows, S_e, S_q, st);
+        default: return launch_step_t<D, 8>(a, s, rows, S_e, S_q, st);
+    }
+}
+
+hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
+                              hipStream_t st) {
+    return d == 128 ? launch_step_d<128>(G, a, s, rows, S_e, S_q, st) : launch_step_d<64>(G, a, s, rows, S_e, S_q, st);
 }
 
 // merge: run combine_kernel over the St partial slots after this launch (unless direct).

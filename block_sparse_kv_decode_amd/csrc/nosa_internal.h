@@ -44,6 +44,7 @@ struct SelectArgs {
     int parts;            // workgroups per row
     int blocks_per_part;
     int scores_only;      // 1: stop after writing block scores
+    int no_pick;          // 1: multi-part plan without the Gamma_q kernel (the fused decode step ranks it)
     int scores_stride;
 };
 
@@ -110,5 +111,9 @@ hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t st);
 hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st);
 hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge);
+// bf16 decode step after a no_pick selection launch: attention over Gamma_e (S_e splits per row) and
+// over Gamma_q ranked in the same launch (S_q splits), then the merge of the S_e + S_q partials.
+hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
+                              hipStream_t st);
 
 }  // namespace nosa

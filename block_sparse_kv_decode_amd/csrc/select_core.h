@@ -1,0 +1,350 @@
+// select_core.h -- the selection machinery shared by the selection kernels and the fused decode
+// step: exact top-k on 64-bit keys, the query-agnostic subset under strict eviction, the
+// query-aware subset, and the compaction of the outputs.  The method and the algorithms are
+// described at the top of select.hip.
+#pragma once
+
+#include "nosa_device.h"
+#include "nosa_internal.h"
+
+namespace nosa {
+
+namespace {
+
+constexpr int kUnroll = 4;           // groups of eight sub-blocks per wave kept in flight
+constexpr int kRankMaxBlocks = 512;  // rows up to this length use the one-pass rank selection
+constexpr int kCandMax = 512;        // candidates kept after the chunk-maximum bound
+constexpr int kEvPre = 4;            // eviction scores prefetched per thread
+constexpr int kEvLdsMax = 4096;      // rows up to this length keep their eviction scores in LDS
+constexpr int kKeyScratch = 256 + kCandMax;   // uint64 LDS entries of the top-k scratch
+
+template <int NT>
+struct SelectShared {
+    uint32_t hist[256];
+    int scan[NT / 64];
+    int bcast[4];
+};
+
+// Inclusive sum over the NT threads of the workgroup, in thread order (all threads call it).
+template <int NT>
+__device__ __forceinline__ int block_incl_scan(int v, int *ws) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) ws[w] = v;
+    __syncthreads();
+    if (NW > 1 && w == 0) {
+        int t = lane < NW ? ws[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) {
+            const int u = __shfl_up(t, o, 64);
+            if (lane >= o) t += u;
+        }
+        if (lane < NW) ws[lane] = t;   // inclusive prefix of the wave totals
+    }
+    __syncthreads();
+    const int add = w > 0 ? ws[w - 1] : 0;
+    __syncthreads();
+    return v + add;
+}
+
+__device__ __forceinline__ uint64_t composite_key(uint32_t k, int id) {
+    return ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+// Radix select over 32-bit keys: marks the kk best candidates; equal keys go to the lowest ids.
+template <int NT, class KeyF, class CandF>
+__device__ void topk_radix(int n, int kk, KeyF key, CandF cand, uint8_t *mark, SelectShared<NT> &sh) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0;
+    int need = kk;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        if (tid < 256) sh.hist[tid] = 0u;
+        if (tid == 0) { sh.bcast[0] = 0; sh.bcast[1] = 0; }
+        __syncthreads();
+        for (int i = tid; i < n; i += NT) {
+            if (cand(i)) {
+                const uint32_t kv = key(i);
+                if ((kv & pmask) == prefix) atomicAdd(&sh.hist[(kv >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        const int cnt = tid < 256 ? (int)sh.hist[255 - tid] : 0;
+        const int ge = block_incl_scan<NT>(cnt, sh.scan);   // candidates with digit >= 255 - tid
+        const int gt = ge - cnt;
+        if (tid < 256 && gt < need && need <= ge) { sh.bcast[0] = 255 - tid; sh.bcast[1] = gt; }
+        __syncthreads();
+        prefix |= (uint32_t)sh.bcast[0] << shift;
+        pmask |= 0xFFu << shift;
+        need -= sh.bcast[1];
+        __syncthreads();
+    }
+    // prefix is the kk-th largest key; take every larger key and the `need` lowest ids equal to it.
+    const uint32_t T = prefix;
+    const int per = (n + NT - 1) / NT;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int eq = 0;
+    for (int i = lo; i < hi; ++i)
+        if (cand(i) && key(i) == T) ++eq;
+    int rank = block_incl_scan<NT>(eq, sh.scan) - eq;
+    for (int i = lo; i < hi; ++i) {
+        if (!cand(i)) continue;
+        const uint32_t kv = key(i);
+        if (kv > T) {
+            mark[i] = 1;
+        } else if (kv == T) {
+            if (rank < need) mark[i] = 1;
+            ++rank;
+        }
+    }
+    __syncthreads();
+}
+
+// Marks the kk largest of the m unique keys buf[0..m) (zeros are empty slots): several lanes of a
+// wave count, for one key, the keys above it and add their counts with lane swaps, so a row of m
+// keys costs m * m / NT comparisons per thread.  mark_id(i, key, rank) is called for each winner.
+template <int NT, class MarkF>
+__device__ __forceinline__ void rank_mark(const uint64_t *buf, int m, int kk, MarkF mark_id) {
+    int tpc = 1;                                     // lanes per key: power of two, <= 64
+    while (tpc < 64 && tpc * 2 * m <= NT) tpc *= 2;
+    const int r = threadIdx.x & (tpc - 1);
+    for (int i = threadIdx.x / tpc; i < m; i += NT / tpc) {
+        const uint64_t ki = buf[i];
+        int cnt = 0;
+        int j = r;
+        for (; j + 7 * tpc < m; j += 8 * tpc) {   // eight independent LDS reads in flight
+            const uint64_t b0 = buf[j], b1 = buf[j + tpc], b2 = buf[j + 2 * tpc], b3 = buf[j + 3 * tpc];
+            const uint64_t b4 = buf[j + 4 * tpc], b5 = buf[j + 5 * tpc], b6 = buf[j + 6 * tpc], b7 = buf[j + 7 * tpc];
+            cnt += (b0 > ki) + (b1 > ki) + (b2 > ki) + (b3 > ki) + (b4 > ki) + (b5 > ki) + (b6 > ki) + (b7 > ki);
+        }
+        for (; j < m; j += tpc) cnt += buf[j] > ki ? 1 : 0;
+        for (int o = 1; o < tpc; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+        if (r == 0 && ki != 0ull && cnt < kk) mark_id(i, ki, cnt);
+    }
+}
+
+// Marks the kk best candidates (key descending, id ascending) in mark[0..n).  Keys are made
+// unique by appending the inverted block id (composite_key), so the kk-th best is well defined.
+//   n <= 512 : every candidate is ranked against all others (rank_mark).
+//   n  > 512 : the row is cut into 256 chunks; the kk-th best chunk maximum is a lower bound T0 of
+//              the kk-th best key overall (the kk best maxima are distinct keys >= T0), and at
+//              most kk chunks hold keys >= T0, so at most kk * chunk candidates survive; they are
+//              gathered and ranked.  When more than kCandMax survive, a radix select takes over.
+// keybuf: LDS scratch of 256 + kCandMax uint64.
+template <int NT, class KeyF, class CandF>
+__device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, uint64_t *keybuf, SelectShared<NT> &sh) {
+    if (kk <= 0) return;
+    const int tid = threadIdx.x;
+    if (n <= kRankMaxBlocks) {
+        for (int i = tid; i < n; i += NT) keybuf[i] = cand(i) ? composite_key(key(i), i) : 0ull;
+        __syncthreads();
+        rank_mark<NT>(keybuf, n, kk, [&](int i, uint64_t, int) { mark[i] = 1; });
+        __syncthreads();
+        return;
+    }
+    constexpr int kChunks = 256;
+    constexpr int TPCH = NT / kChunks;              // threads per chunk (adjacent lanes)
+    uint64_t *tmax = keybuf;                        // [256] chunk maxima
+    uint64_t *cbuf = keybuf + kChunks;              // [kCandMax] surviving candidates
+    const int csize = (n + kChunks - 1) / kChunks;
+    {
+        const int ch = tid / TPCH, part = tid - ch * TPCH;
+        const int lo = min(n, ch * csize), hi = min(n, lo + csize);
+        uint64_t best = 0ull;
+        for (int i = lo + part; i < hi; i += TPCH)
+            if (cand(i)) {
+                const uint64_t c = composite_key(key(i), i);
+                best = c > best ? c : best;
+            }
+        for (int o = 1; o < TPCH; o <<= 1) {
+            const uint64_t other = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), o, 64) << 32) |
+                                   (uint32_t)__shfl_xor((int)(uint32_t)best, o, 64);
+            best = other > best ? other : best;
+        }
+        if (part == 0) tmax[ch] = best;
+        if (tid == 0) cbuf[0] = 1ull;   // T0 when fewer than kk chunks hold a candidate: keep all
+    }
+    __syncthreads();
+    // threshold T0: the kk-th best chunk maximum (the maximum ranked kk - 1)
+    rank_mark<NT>(tmax, kChunks, kk, [&](int, uint64_t ki, int rank) {
+        if (rank == kk - 1) cbuf[0] = ki;
+    });
+    __syncthreads();
+    const uint64_t T0 = cbuf[0];
+    __syncthreads();
+    const int per = (n + NT - 1) / NT;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int cnt = 0;
+    for (int i = lo; i < hi; ++i)
+        if (cand(i) && composite_key(key(i), i) >= T0) ++cnt;
+    const int incl = block_incl_scan<NT>(cnt, sh.scan);
+    if (tid == NT - 1) sh.bcast[2] = incl;
+    __syncthreads();
+    const int total = sh.bcast[2];
+    if (total <= kCandMax) {
+        int pos = incl - cnt;
+        for (int i = lo; i < hi; ++i)
+            if (cand(i)) {
+                const uint64_t c = composite_key(key(i), i);
+                if (c >= T0) cbuf[pos++] = c;
+            }
+        __syncthreads();
+        rank_mark<NT>(cbuf, total, kk, [&](int, uint64_t c, int) { mark[0xFFFFFFFFu - (uint32_t)c] = 1; });
+        __syncthreads();
+        return;
+    }
+    topk_radix<NT>(n, kk, key, cand, mark, sh);
+}
+
+// Writes, in ascending id, the ids i < n with inE[i] to agn[0..ke) and those with inE[i] | inQ[i]
+// to sel[0..k), padding with -1: one scan over packed (agnostic, selected) counts.
+template <int NT>
+__device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, int32_t *agn, int ke, int32_t *sel,
+                                int k, SelectShared<NT> &sh) {
+    const int tid = threadIdx.x;
+    const int per = (n + NT - 1) / NT;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int cnt = 0;   // low 16 bits: selected; high 16 bits: agnostic
+    for (int i = lo; i < hi; ++i) cnt += ((inE[i] | inQ[i]) != 0 ? 1 : 0) + (inE[i] != 0 ? 0x10000 : 0);
+    const int incl = block_incl_scan<NT>(cnt, sh.scan);
+    int ps = (incl - cnt) & 0xFFFF, pe = (incl - cnt) >> 16;
+    for (int i = lo; i < hi; ++i) {
+        if (inE[i]) {
+            if (agn && pe < ke) agn[pe] = i;
+            ++pe;
+        }
+        if (inE[i] | inQ[i]) {
+            if (ps < k) sel[ps] = i;
+            ++ps;
+        }
+    }
+    if (tid == NT - 1) sh.bcast[2] = incl;
+    __syncthreads();
+    const int ns = sh.bcast[2] & 0xFFFF, ne = sh.bcast[2] >> 16;
+    for (int p = ns + tid; p < k; p += NT) sel[p] = -1;
+    if (agn)
+        for (int p = ne + tid; p < ke; p += NT) agn[p] = -1;
+}
+
+// LDS layout of the selection phase for a row of n blocks.
+struct RowLds {
+    uint64_t *keys;     // [kKeyScratch] top-k scratch
+    float *sc;          // [n] block scores
+    float *ev;          // [n] eviction scores, or nullptr (then read from global)
+    uint8_t *inE;       // [n]
+    uint8_t *inQ;       // [n]
+};
+
+template <int NT>
+__host__ __device__ inline bool ev_in_lds(int n) { return n <= kEvLdsMax; }
+
+template <int NT>
+__host__ __device__ inline size_t row_lds_bytes(int n) {
+    const size_t n16 = (size_t)((n + 15) & ~15);
+    return 8 * (size_t)kKeyScratch + 4 * n16 + (ev_in_lds<NT>(n) ? 4 * n16 : 0) + 2 * n16;
+}
+
+template <int NT>
+__device__ inline RowLds carve(unsigned char *dyn, int n) {
+    const int n16 = (n + 15) & ~15;
+    RowLds L;
+    unsigned char *p = dyn;
+    L.keys = (uint64_t *)p;
+    p += 8 * kKeyScratch;
+    L.sc = (float *)p;
+    p += 4 * n16;
+    L.ev = nullptr;
+    if (ev_in_lds<NT>(n)) {
+        L.ev = (float *)p;
+        p += 4 * n16;
+    }
+    L.inE = p;
+    L.inQ = p + n16;
+    return L;
+}
+
+// Loads up to kEvPre * NT eviction scores of the row into registers (issued early; stored to
+// LDS by ev_store once they are needed, together with the rest of a row of up to kEvLdsMax
+// blocks).  Longer rows read their eviction scores from global memory during the top-k.
+template <int NT>
+__device__ __forceinline__ void ev_load(const SelectArgs &a, int row, float (&e)[kEvPre]) {
+    const float *evr = a.ev + (size_t)row * a.n_blocks_max;
+#pragma unroll
+    for (int r = 0; r < kEvPre; ++r) {
+        const int i = threadIdx.x + r * NT;
+        e[r] = i < a.n_blocks ? evr[i] : 0.0f;
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void ev_store(const SelectArgs &a, int row, const RowLds &L, int n,
+                                         const float (&e)[kEvPre]) {
+    if (!L.ev) return;
+#pragma unroll
+    for (int r = 0; r < kEvPre; ++r) {
+        const int i = threadIdx.x + r * NT;
+        if (i < n) L.ev[i] = e[r];
+    }
+    // the rest of a long row (beyond the prefetch): independent loads, several in flight
+    const float *evr = a.ev + (size_t)row * a.n_blocks_max;
+#pragma unroll 4
+    for (int i = threadIdx.x + kEvPre * NT; i < n; i += NT) L.ev[i] = evr[i];
+}
+
+// Gamma_e of one row into L.inE (all threads of the workgroup): the sink and window blocks plus
+// the score-ranked members under strict eviction.  Reads the previous Gamma_e from agn_state; uses
+// L.inQ as scratch and leaves it cleared.
+template <int NT>
+__device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh) {
+    const int tid = threadIdx.x;
+    const int n = a.n_blocks;
+    for (int i = tid; i < n; i += NT) {
+        L.inE[i] = 0;
+        L.inQ[i] = 0;
+    }
+    __syncthreads();
+    const int n_prev = a.n_prev;
+    const bool fresh = (n_prev == 0);
+    const int w_lo = n - a.n_window;              // first window block
+    const int left = n_prev - a.n_window;         // blocks below this were ranked (or out) last step
+    if (!fresh)
+        for (int j = tid; j < a.ke; j += NT) {
+            const int id = a.agn[(size_t)row * a.ke + j];
+            if (id >= 0 && id < n_prev) L.inQ[id] = 1;   // previous Gamma_e (inQ reused as scratch)
+        }
+    for (int i = tid; i < n; i += NT)
+        if (i < a.n_sink || i >= w_lo) L.inE[i] = 1;
+    __syncthreads();
+    const float *evg = a.ev + (size_t)row * a.n_blocks_max;
+    const float *evl = L.ev;
+    const uint8_t *prevE = L.inQ;
+    const int n_sink = a.n_sink;
+    topk_mark<NT>(
+        n, a.ke - a.n_sink - a.n_window, [&](int i) { return order_key(evl ? evl[i] : evg[i]); },
+        [&](int i) { return i >= n_sink && i < w_lo && (fresh || i >= left || prevE[i]); }, L.inE, L.keys, sh);
+    for (int i = tid; i < n; i += NT) L.inQ[i] = 0;
+    __syncthreads();
+}
+
+// Gamma_q of one row from the block scores in L.sc and Gamma_e in L.inE, then the outputs in
+// ascending block id: the selection, and agn_state when write_agn is set.
+template <int NT>
+__device__ void select_query(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh, bool write_agn) {
+    const int n = a.n_blocks;
+    const uint8_t *inE = L.inE;
+    const float *sc = L.sc;
+    topk_mark<NT>(
+        n, a.kq, [&](int i) { return order_key(sc[i]); }, [&](int i) { return !inE[i]; }, L.inQ, L.keys, sh);
+    const int k = a.kq + a.ke;
+    compact_outputs<NT>(n, L.inE, L.inQ, (write_agn && a.ke > 0) ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
+                        a.sel + (size_t)row * k, k, sh);
+}
+
+}  // namespace
+
+}  // namespace nosa

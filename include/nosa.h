@@ -13,6 +13,7 @@
  *   3. (offloaded KV only) hit/miss check against the GPU block cache, replacement map and
  *      host-to-GPU copy of the missed blocks                  -> nosa_cache_update ([P1] §4, App. A)
  *   4. GQA attention over the tokens of the selected blocks  -> nosa_sparse_decode ([P1] App. A)
+ *   1+2+4 in one call on GPU-resident KV                     -> nosa_decode_step
  *   3+4 fused for offloaded KV, with the copy of the missed blocks overlapped with attention over
  *      the blocks already cached                             -> nosa_offload_decode ([P1] §4, App. A)
  * Pooled keys (sub-block means) are state kept next to the KV cache -> nosa_pool_keys ([P1] §3.1),
@@ -223,6 +224,22 @@ int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t 
 int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store,
                        const void *v_store, int32_t store_blocks, const int32_t *block_table,
                        float softmax_scale, void *out, void *ws, hipStream_t stream);
+
+/*
+ * One whole decode step on GPU-resident KV: nosa_select followed by nosa_sparse_decode over the
+ * selection ([P1] App. A: select, then attend; §2.1 and §3.1 for the selection).  Arguments as for
+ * the two calls (table = selected).  agn_state, selected and out come out as from the two calls:
+ * selected and agn_state exactly, out up to float32 summation order.  When the selection would
+ * score a row in several workgroups and rank Gamma_q in a kernel of its own (rows of more than
+ * 64 KiB of pooled keys and fewer than 256 rows; bf16; kq, ke > 0; n_blocks <= 512), the ranking
+ * moves into the attention launch instead: the splits over Gamma_e start at once, and each split
+ * over Gamma_q ranks the row's Gamma_q itself, so the ranking hides under attention.  Otherwise the
+ * step is the two calls.  The workspace is that of nosa_workspace_bytes.
+ */
+int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                     int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, const void *k_store,
+                     const void *v_store, int32_t store_blocks, float softmax_scale, void *out, void *ws,
+                     hipStream_t stream);
 
 /*
  * Transfer at a chosen granularity ([P1] §3.2: block-wise against element-wise communication;

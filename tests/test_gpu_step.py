@@ -1,0 +1,111 @@
+"""Parity of the one-call decode step (nosa_decode_step) with the oracle and with nosa_select +
+nosa_sparse_decode: the fused path (Gamma_q ranked inside the attention launch) on row shapes that
+take it, with sink / window blocks and with arrivals across steps, and the fallback on shapes that
+do not (fp32, one subset empty, short rows, many rows)."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import block_sparse_kv_decode_amd as N  # noqa: E402
+from nosa_inputs import f32_to_bf16_bits, generate, small_workload  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from tests import gpuhelp as H  # noqa: E402
+
+CASES = {
+    # fused: fewer than 256 rows, rows above 64 KiB of pooled keys, bf16, kq and ke > 0
+    "fused_g4": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=150, n_blocks_max=160, kq=20,
+                     ke=12, seed=51),
+    "fused_g8_ragged": dict(batch=3, n_q_heads=8, n_kv_heads=1, head_dim=128, n_blocks=301, kq=37, ke=29, seed=52),
+    "fused_d64_g2": dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_blocks=500, kq=40, ke=24, seed=53),
+    "fallback_long_rows": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=700, kq=20, ke=20,
+                               seed=62),
+    "fused_sink_window": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=200, kq=16, ke=48,
+                              n_sink=1, n_window=16, seed=54),
+    # fallback: fp32, an empty subset, short rows, many rows
+    "fallback_f32": dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_blocks=300, kq=8, ke=8, dtype="f32",
+                         seed=55),
+    "fallback_kq0": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=150, kq=0, ke=24, seed=56),
+    "fallback_ke0": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=150, kq=24, ke=0, seed=57),
+    "fallback_short": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=40, kq=6, ke=6, seed=58),
+    "fallback_many_rows": dict(batch=64, n_q_heads=8, n_kv_heads=4, head_dim=128, n_blocks=20, kq=4, ke=4, seed=59),
+}
+
+
+def _two_calls(shape, q, kp, ev, n_prev, agn_in, k, v, nbmax, ws):
+    agn = agn_in.clone()
+    R = shape.batch * shape.n_kv_heads
+    sel = torch.full((R, shape.kq + shape.ke), -7, dtype=torch.int32, device="cuda")
+    N.nosa_select(shape, q, kp, ev, n_prev, agn, sel, ws)
+    out = H.gpu_decode(shape, q, k, v, nbmax, sel, ws)
+    return sel, agn, out
+
+
+def _step(shape, q, kp, ev, n_prev, agn_in, k, v, nbmax, ws):
+    agn = agn_in.clone()
+    R = shape.batch * shape.n_kv_heads
+    sel = torch.full((R, shape.kq + shape.ke), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((shape.batch, shape.n_q_heads, shape.head_dim), float("nan"), dtype=q.dtype, device="cuda")
+    N.nosa_decode_step(shape, q, kp, ev, n_prev, agn, sel, k, v, nbmax, 1.0 / np.sqrt(shape.head_dim), out, ws)
+    return sel, agn, out
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_step_matches_two_calls_and_oracle(name):
+    w = small_workload(name, **CASES[name])
+    ns, nw = w.n_sink, w.n_window
+    x = generate(w)
+    shape = H.shape_of(w)
+    q, k, v, ev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
+    kp = H.gpu_pool(shape, k)
+    ws = N.workspace(shape)
+    R = w.rows
+    agn0 = torch.full((R, max(w.ke, 1)), -7, dtype=torch.int32, device="cuda")
+    sel_a, agn_a, out_a = _two_calls(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    sel_b, agn_b, out_b = _step(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b) and torch.equal(agn_a[:, :w.ke], agn_b[:, :w.ke])
+    kp_ref = O.pool_keys(x["k"], 32)
+    s_ref = O.block_scores(x["q"], kp_ref, w.n_blocks, 2)
+    H.check_selection(H.host(sel_b), H.host(agn_b), s_ref, x["evict"], w.kq, w.ke, n_sink=ns, n_window=nw)
+    ref = O.attention(x["q"], x["k"], x["v"], H.host(sel_b).reshape(w.batch, w.n_kv_heads, w.k))
+    print(name, H.check_attention(H.host(out_b), ref, w.dtype, name + " (one call)"))
+    H.check_attention(H.host(out_a), ref, w.dtype, name + " (two calls)")
+    # repeatable bit for bit
+    sel_c, _, out_c = _step(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_b, sel_c)
+    assert torch.equal(out_b.view(torch.int16) if out_b.dtype == torch.bfloat16 else out_b,
+                       out_c.view(torch.int16) if out_c.dtype == torch.bfloat16 else out_c)
+
+
+def test_decode_step_multistep_with_arrivals():
+    # Strict eviction across steps through the one-call step: Gamma_e follows the oracle exactly,
+    # selections within the tie band, attention within tolerance, at every step.
+    w = small_workload("step_multi", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=120,
+                       n_blocks_max=140, kq=14, ke=18, seed=60)
+    x = generate(w)
+    shape0 = H.shape_of(w)
+    k, v, ev = H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
+    kp = H.gpu_pool(shape0, k)
+    ws = N.workspace(shape0)
+    kp_ref = O.pool_keys(x["k"], 32)
+    rng = np.random.default_rng(61)
+    qf = x["q"]
+    n, agn, agn_ref = 120, torch.zeros((w.rows, w.ke), dtype=torch.int32, device="cuda"), None
+    for t in range(8):
+        n_prev = 0 if t == 0 else n
+        if t in (2, 3, 6):
+            n += 3
+        shape = shape0.copy(n_blocks=n)
+        sel, agn_new, out = _step(shape, H.dev(qf), kp, ev, n_prev, agn, k, v, w.nbmax, ws)
+        torch.cuda.synchronize()
+        s_ref = O.block_scores(qf, kp_ref[:, :, :2 * n], n, 2)
+        H.check_selection(H.host(sel), H.host(agn_new), s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
+        ref = O.attention(qf, x["k"], x["v"], H.host(sel).reshape(w.batch, w.n_kv_heads, w.k))
+        H.check_attention(H.host(out), ref, "bf16", "step %d" % t)
+        _, agn_ref, _ = O.select(s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
+        agn = agn_new
+        qf = f32_to_bf16_bits((H.as_f64(qf) + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32))
