@@ -327,10 +327,12 @@ int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst
 }
 
 // The selection launch(es).  no_pick: the multi-part plan stops after scoring and Gamma_e (the
-// fused decode step ranks Gamma_q); *used receives the launch descriptor when not NULL.
+// fused decode step ranks Gamma_q); *used receives the launch descriptor when not NULL; with
+// describe_only nothing is launched (the one-workgroup-per-row step runs the selection itself).
 static int run_scores(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
                       int32_t n_prev, int32_t *agn_state, int32_t *selected, float *scores_out, void *ws,
-                      hipStream_t stream, bool no_pick = false, SelectArgs *used = nullptr) {
+                      hipStream_t stream, bool no_pick = false, SelectArgs *used = nullptr,
+                      bool describe_only = false) {
     const bool scores_only = scores_out != nullptr;
     REQUIRE_PTR(q, 16);
     REQUIRE_PTR(pooled_k, 16);
@@ -372,6 +374,7 @@ static int run_scores(const nosa_shape *shape, const void *q, const float *poole
     a.no_pick = no_pick ? 1 : 0;
     a.scores_stride = shape->n_blocks_max;
     if (used) *used = a;
+    if (describe_only) return NOSA_OK;
     hipError_t e = launch_select(shape->dtype, shape->head_dim, spb_of(shape), a, rows_of(shape), pp.threads,
                                   pp.part_threads, stream);
     return e == hipSuccess ? ok() : hip_fail(e, scores_only ? "block_scores launch" : "select launch");
@@ -574,6 +577,20 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
     // Gamma_q kernel (multi-part plan), for bf16 rows with both subsets non-empty.
     const bool fused = shape->dtype == NOSA_BF16 && pp.P > 1 && shape->kq > 0 && shape->ke > 0 &&
                        shape->n_blocks <= kStepMaxBlocks;
+    // One workgroup per row does it all when it would both score-and-select the row and attend it
+    // in a single split anyway.
+    const bool row_fused = shape->dtype == NOSA_BF16 && pp.P == 1 && pp.threads == 256 && dp.S == 1;
+    if (row_fused) {
+        SelectArgs sa;
+        if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream,
+                             false, &sa, true)))
+            return rc;
+        DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
+        a.table = selected;
+        hipError_t e = launch_row_step(shape->head_dim, group_of(shape), spb_of(shape), a, sa, rows_of(shape),
+                                       stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "decode_step launch");
+    }
     if (!fused) {
         if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream)))
             return rc;

@@ -492,6 +492,30 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
     decode_mfma_split<D, G>(a, row, sp, qlist, 1, j0, j1, sh);
 }
 
+// ---- the decode step in one workgroup per row ----------------------------------------------
+// Grid rows, bf16, for plans where one 256-thread workgroup scores and selects a row and a single
+// split attends it (many rows, short rows): the workgroup scores its row, selects (writing
+// agn_state and the selection), and attends the selected blocks straight after, so each row's
+// attention starts when its own selection is done rather than when the slowest row's is.
+template <int D, int G, int SPB>
+__global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectArgs s) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ SplitShared<D, G> sh;
+    __shared__ SelectShared<256> ssh;
+    const int row = blockIdx.x;
+    const RowLds L = carve<256>(dyn, s.n_blocks);
+    float e[kEvPre];
+    ev_load<256>(s, row, e);
+    score_range<uint16_t, D, SPB, 256>(s, row, 0, s.n_blocks, L.sc, nullptr);
+    ev_store<256>(s, row, L, s.n_blocks, e);
+    __syncthreads();
+    select_agnostic<256>(s, row, L, ssh);
+    select_query<256>(s, row, L, ssh, true);
+    __syncthreads();   // this workgroup's selection, written to global memory, is visible to it
+    const int k = s.kq + s.ke;
+    decode_mfma_split<D, G>(a, row, 0, s.sel + (size_t)row * k, 1, 0, k, sh);
+}
+
 // Merges the St split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
 // Empty partials (max = -inf) carry nothing and are passed over.
 template <typename T, int D, int G>
@@ -568,6 +592,44 @@ static hipError_t launch_step_d(int G, const DecodeArgs &a, const SelectArgs &s,
 hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
                               hipStream_t st) {
     return d == 128 ? launch_step_d<128>(G, a, s, rows, S_e, S_q, st) : launch_step_d<64>(G, a, s, rows, S_e, S_q, st);
+}
+
+template <int D, int G, int SPB>
+static hipError_t launch_row_step_t(const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st) {
+    const size_t dyn = row_lds_bytes<256>(s.n_blocks);
+    if (dyn > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)row_step_kernel<D, G, SPB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    row_step_kernel<D, G, SPB><<<dim3((unsigned)rows), dim3(256), dyn, st>>>(a, s);
+    return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_row_step_g(int spb, const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st) {
+    switch (spb) {
+        case 1: return launch_row_step_t<D, G, 1>(a, s, rows, st);
+        case 2: return launch_row_step_t<D, G, 2>(a, s, rows, st);
+        case 4: return launch_row_step_t<D, G, 4>(a, s, rows, st);
+        default: return launch_row_step_t<D, G, 8>(a, s, rows, st);
+    }
+}
+
+template <int D>
+static hipError_t launch_row_step_d(int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
+                                    hipStream_t st) {
+    switch (G) {
+        case 1: return launch_row_step_g<D, 1>(spb, a, s, rows, st);
+        case 2: return launch_row_step_g<D, 2>(spb, a, s, rows, st);
+        case 4: return launch_row_step_g<D, 4>(spb, a, s, rows, st);
+        default: return launch_row_step_g<D, 8>(spb, a, s, rows, st);
+    }
+}
+
+hipError_t launch_row_step(int d, int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
+                           hipStream_t st) {
+    return d == 128 ? launch_row_step_d<128>(G, spb, a, s, rows, st) : launch_row_step_d<64>(G, spb, a, s, rows, st);
 }
 
 // merge: run combine_kernel over the St partial slots after this launch (unless direct).

@@ -115,5 +115,8 @@ hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows,
 // over Gamma_q ranked in the same launch (S_q splits), then the merge of the S_e + S_q partials.
 hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
                               hipStream_t st);
+// bf16 decode step in one workgroup per row: scoring, selection and single-split attention.
+hipError_t launch_row_step(int d, int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
+                           hipStream_t st);
 
 }  // namespace nosa

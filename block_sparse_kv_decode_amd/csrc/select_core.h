@@ -1,6 +1,6 @@
 // select_core.h -- the selection machinery shared by the selection kernels and the fused decode
-// step: exact top-k on 64-bit keys, the query-agnostic subset under strict eviction, the
-// query-aware subset, and the compaction of the outputs.  The method and the algorithms are
+// steps: exact top-k on 64-bit keys, the query-agnostic subset under strict eviction, the
+// query-aware subset, the compaction of the outputs, and the pooled-key scoring of a row range.  The method and the algorithms are
 // described at the top of select.hip.
 #pragma once
 
@@ -343,6 +343,85 @@ __device__ void select_query(const SelectArgs &a, int row, const RowLds &L, Sele
     const int k = a.kq + a.ke;
     compact_outputs<NT>(n, L.inE, L.inQ, (write_agn && a.ke > 0) ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
                         a.sel + (size_t)row * k, k, sh);
+}
+
+
+// qs slice of this lane: float4 chunks c8 + 8 i of sum_h q[b][g*G + h].
+template <typename T, int D>
+__device__ __forceinline__ void group_query(const SelectArgs &a, int b, int g, int c8, float4 (&qv)[D / 32]) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) qv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h = 0; h < a.G; ++h) {
+        const size_t base = (size_t)(b * a.Hq + g * a.G + h) * D;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            const size_t e0 = base + (size_t)(c8 + 8 * i) * 4;
+            if (sizeof(T) == 2) {
+                const uint2 u = *(const uint2 *)((const uint16_t *)a.q + e0);
+                qv[i].x += bf16_lo(u.x);
+                qv[i].y += bf16_hi(u.x);
+                qv[i].z += bf16_lo(u.y);
+                qv[i].w += bf16_hi(u.y);
+            } else {
+                const float4 f = *(const float4 *)((const float *)a.q + e0);
+                qv[i].x += f.x;
+                qv[i].y += f.y;
+                qv[i].z += f.z;
+                qv[i].w += f.w;
+            }
+        }
+    }
+}
+
+// Scores blocks [blk_lo, blk_hi) of one row; writes them to LDS (sc) or global (gscore).
+template <typename T, int D, int SPB, int NT>
+__device__ __forceinline__ void score_range(const SelectArgs &a, int row, int blk_lo, int blk_hi, float *sc,
+                                            float *gscore) {
+    constexpr int CPLS = D / 32;   // 16-byte chunks per lane of one fp32 sub-block row
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
+    const int r8 = lane >> 3, c8 = lane & 7;
+    const int sb_lo = blk_lo * SPB, sb_hi = blk_hi * SPB;
+    const int ngroups = (sb_hi - sb_lo + 7) >> 3;   // groups of 8 sub-blocks
+    const float *kprow = a.kp + (size_t)row * a.n_blocks_max * SPB * D;
+    float4 qv[CPLS];
+    group_query<T, D>(a, b, g, c8, qv);
+    for (int g0 = w; g0 < ngroups; g0 += NW * kUnroll) {
+        float4 x[kUnroll][CPLS];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = sb_lo + (g0 + NW * u) * 8 + r8;
+            const bool v = (g0 + NW * u < ngroups) && (j < sb_hi);
+#pragma unroll
+            for (int i = 0; i < CPLS; ++i)
+                x[u][i] = v ? *(const float4 *)(kprow + (size_t)j * D + (c8 + 8 * i) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = sb_lo + (g0 + NW * u) * 8 + r8;
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPLS; ++i) {
+                s = fmaf(x[u][i].x, qv[i].x, s);
+                s = fmaf(x[u][i].y, qv[i].y, s);
+                s = fmaf(x[u][i].z, qv[i].z, s);
+                s = fmaf(x[u][i].w, qv[i].w, s);
+            }
+            s += dpp<kDppQuadXor1>(s);
+            s += dpp<kDppQuadXor2>(s);
+            s += dpp<kDppRowHalfMirror>(s);     // every lane of the 8-lane group holds u[j]
+            if (SPB >= 2) s = fmaxf(s, dpp<kDppRowMirror>(s));
+            if (SPB >= 4) s = fmaxf(s, xor_lane(s, 16));
+            if (SPB >= 8) s = fmaxf(s, xor_lane(s, 32));
+            const bool v = (g0 + NW * u < ngroups) && (j < sb_hi);
+            if (v && (lane % (8 * SPB)) == 0) {
+                const int blk = j / SPB;
+                if (sc) sc[blk] = s;
+                else gscore[blk] = s;
+            }
+        }
+    }
 }
 
 }  // namespace

@@ -1,7 +1,8 @@
 """Parity of the one-call decode step (nosa_decode_step) with the oracle and with nosa_select +
 nosa_sparse_decode: the fused path (Gamma_q ranked inside the attention launch) on row shapes that
-take it, with sink / window blocks and with arrivals across steps, and the fallback on shapes that
-do not (fp32, one subset empty, short rows, many rows)."""
+take it, with sink / window blocks and with arrivals across steps; the one-workgroup-per-row step
+on shapes with enough rows for a single split each; and the two calls on shapes that take neither
+(fp32, one subset empty, short rows, long rows)."""
 
 import numpy as np
 import pytest
@@ -30,7 +31,18 @@ CASES = {
     "fallback_kq0": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=150, kq=0, ke=24, seed=56),
     "fallback_ke0": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=150, kq=24, ke=0, seed=57),
     "fallback_short": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=40, kq=6, ke=6, seed=58),
-    "fallback_many_rows": dict(batch=64, n_q_heads=8, n_kv_heads=4, head_dim=128, n_blocks=20, kq=4, ke=4, seed=59),
+    # one workgroup per row scores, selects and attends (256 rows or more, single split): GQA
+    # groups 1 to 8, d 64 and 128, ragged budgets, an empty subset, sink / window blocks, long rows
+    "rowstep_many_rows": dict(batch=64, n_q_heads=8, n_kv_heads=4, head_dim=128, n_blocks=20, kq=4, ke=4, seed=59),
+    "rowstep_g8_ragged": dict(batch=128, n_q_heads=16, n_kv_heads=2, head_dim=128, n_blocks=77, kq=9, ke=5,
+                              seed=63),
+    "rowstep_g1_d64": dict(batch=64, n_q_heads=4, n_kv_heads=4, head_dim=64, n_blocks=50, kq=7, ke=6, seed=64),
+    "rowstep_sink_window": dict(batch=64, n_q_heads=8, n_kv_heads=4, head_dim=64, n_blocks=100, kq=5, ke=10,
+                                n_sink=1, n_window=4, seed=65),
+    "rowstep_kq0": dict(batch=64, n_q_heads=16, n_kv_heads=4, head_dim=128, n_blocks=30, kq=0, ke=8, seed=66),
+    "rowstep_ke0": dict(batch=64, n_q_heads=16, n_kv_heads=4, head_dim=128, n_blocks=30, kq=8, ke=0, seed=67),
+    "rowstep_long_rows": dict(batch=32, n_q_heads=16, n_kv_heads=8, head_dim=128, n_blocks=1500, kq=8, ke=7,
+                              seed=68),
 }
 
 
@@ -81,11 +93,17 @@ def test_decode_step_matches_two_calls_and_oracle(name):
                        out_c.view(torch.int16) if out_c.dtype == torch.bfloat16 else out_c)
 
 
-def test_decode_step_multistep_with_arrivals():
+MULTI = {
+    "fused": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kq=14, ke=18, seed=60),
+    "rowstep": dict(batch=64, n_q_heads=16, n_kv_heads=4, head_dim=128, kq=6, ke=9, seed=69),
+}
+
+
+@pytest.mark.parametrize("plan", sorted(MULTI))
+def test_decode_step_multistep_with_arrivals(plan):
     # Strict eviction across steps through the one-call step: Gamma_e follows the oracle exactly,
     # selections within the tie band, attention within tolerance, at every step.
-    w = small_workload("step_multi", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=120,
-                       n_blocks_max=140, kq=14, ke=18, seed=60)
+    w = small_workload("step_multi_" + plan, n_blocks=120, n_blocks_max=140, **MULTI[plan])
     x = generate(w)
     shape0 = H.shape_of(w)
     k, v, ev = H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
