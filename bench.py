@@ -6,7 +6,7 @@ selection) followed by nosa_sparse_decode (split-K GQA attention over the select
 call.  Pooled keys are state built once before timing (they change only when a block fills up).
 tokens/s = batch / step time.
 
-  python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--config C2] [--also C3,F1]
+  python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config C2] [--also C3,F1]
                   [--no-cpu-baseline] [--no-offload] [--no-transfer]
 
 Prints one JSON line.  `value` is the headline workload (bs16 / 16K context by default); the
@@ -31,8 +31,20 @@ sys.path.insert(0, ROOT)
 
 LAYERS = 4   # independent buffer sets the resident step rotates over (see run_resident)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_kernel_c2_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_decode_amd", "csrc", "decode.hip")
+# HBM bytes per launch from rocprofv3 counter runs: the attention call at bs16 / 16K (two kernels)
+# and the one-workgroup-per-row step kernel at bs64 / 4K
+PROFILE_TRAFFIC = {"C2": os.path.join(ROOT, "profiles", "decode_kernel_c2_traffic.json"),
+                   "C3": os.path.join(ROOT, "profiles", "step_kernel_c3_traffic.json")}
+# the sources the attention and step kernels are compiled from
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_kv_decode_amd", "csrc", f)
+               for f in ("decode.hip", "select_core.h", "nosa_device.h", "nosa_internal.h")]
+
+
+def kernel_src_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -526,13 +538,13 @@ def cpu_baseline(cfg, budget_s=10.0, single_s=4.0, max_s=30.0):
 
 
 def traffic_record(cfg):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs, if they were taken on
-    this workload and on the current decode kernel source."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on this
+    workload and on the current kernel sources."""
+    path = PROFILE_TRAFFIC.get(cfg)
+    if path is None or not os.path.exists(path):
         return None
-    rec = json.load(open(PROFILE_TRAFFIC))
-    src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if rec.get("decode_src_sha256") != src_hash or rec.get("workload") != cfg:
+    rec = json.load(open(path))
+    if rec.get("kernel_src_sha256") != kernel_src_sha256() or rec.get("workload") != cfg:
         return None
     return rec.get("bytes_per_launch")
 
@@ -548,8 +560,10 @@ def describe(w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 1000 steps (about 70 ms at bs16 / 16K): the first launches after a synchronisation take a few
+    # hundred microseconds, which 100 steps would spread as several microseconds per step
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--also", default="C3,F1", help="comma list of extra resident workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -627,6 +641,10 @@ def main():
             "step_hbm_frac": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "decode_gbps": b2["decode"] / (r["decode_ms_mean"] * 1e-3) / 1e9,
             "decode_avg_launch_ms": r["decode_ms_mean"], "select_avg_launch_ms": r["select_ms_mean"],
+            "step_ms_median_events": r["step_ms_median"],
+            "step_events_gbps": b2["step"] / (r["step_ms_median"] * 1e-3) / 1e9,
+            # counter-measured HBM bytes of the step kernel, where it is one launch (bs64 / 4K)
+            "step_traffic_bytes": traffic_record(cfg),
         }
     if also:
         line["also"] = also
