@@ -69,6 +69,8 @@ __global__ __launch_bounds__(NT) void score_part_kernel(SelectArgs a) {
         float e[kEvPre];
         ev_load<NT>(a, row, e);
         ev_store<NT>(a, row, L, a.n_blocks, e);
+        // The ranking shares its CU with the scoring workgroups: give it issue priority.
+        __builtin_amdgcn_s_setprio(2);
         select_agnostic<NT>(a, row, L, sh);
         compact_outputs<NT>(a.n_blocks, L.inE, L.inE, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
                             nullptr, 0, sh);

@@ -112,6 +112,25 @@ template <int NT, class MarkF>
 __device__ __forceinline__ void rank_mark(const uint64_t *buf, int m, int kk, MarkF mark_id) {
     int tpc = 1;                                     // lanes per key: power of two, <= 64
     while (tpc < 64 && tpc * 2 * m <= NT) tpc *= 2;
+    if (tpc == 1) {
+        // One lane per key: every lane walks the same keys, so the walk is uniform and sixteen
+        // keys come from one LDS address with immediate offsets (broadcast reads).
+        for (int i = threadIdx.x; i < m; i += NT) {
+            const uint64_t ki = buf[i];
+            int cnt = 0;
+            int j = 0;
+            for (; j + 16 <= m; j += 16) {
+                uint64_t b[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) b[u] = buf[j + u];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) cnt += b[u] > ki ? 1 : 0;
+            }
+            for (; j < m; ++j) cnt += buf[j] > ki ? 1 : 0;
+            if (ki != 0ull && cnt < kk) mark_id(i, ki, cnt);
+        }
+        return;
+    }
     const int r = threadIdx.x & (tpc - 1);
     for (int i = threadIdx.x / tpc; i < m; i += NT / tpc) {
         const uint64_t ki = buf[i];
@@ -219,14 +238,15 @@ __device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, i
             ++pe;
         }
         if (inE[i] | inQ[i]) {
-            if (ps < k) sel[ps] = i;
+            if (sel && ps < k) sel[ps] = i;
             ++ps;
         }
     }
     if (tid == NT - 1) sh.bcast[2] = incl;
     __syncthreads();
     const int ns = sh.bcast[2] & 0xFFFF, ne = sh.bcast[2] >> 16;
-    for (int p = ns + tid; p < k; p += NT) sel[p] = -1;
+    if (sel)
+        for (int p = ns + tid; p < k; p += NT) sel[p] = -1;
     if (agn)
         for (int p = ne + tid; p < ke; p += NT) agn[p] = -1;
 }
