@@ -79,6 +79,29 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// Entries [j0, j1) of a split's block table (tab[j * stride]), held 64 at a time in one register
+// of the wave: lane l holds entry base + l.  id(j) must be called with uniform, non-decreasing j
+// in [j0, j1); crossing into the next 64 entries reloads the window.
+struct TableWindow {
+    const int32_t *tab;
+    int stride, j1, lane, base, v;
+    __device__ __forceinline__ TableWindow(const int32_t *t, int s, int j0, int j1_, int ln)
+        : tab(t), stride(s), j1(j1_), lane(ln), base(j0) {
+        v = fetch();
+    }
+    __device__ __forceinline__ int fetch() const {
+        const int jj = base + lane;
+        return jj < j1 ? tab[(size_t)jj * stride] : -1;
+    }
+    __device__ __forceinline__ int id(int j) {
+        if (j - base >= 64) {
+            base += 64 * ((j - base) >> 6);
+            v = fetch();
+        }
+        return __builtin_amdgcn_readlane(v, j - base);
+    }
+};
+
 // acc[h][e] += p[tok][h] * V[tok][chunk e] over this lane's PV tokens of the block.
 template <typename T, int D, int G>
 __device__ __forceinline__ void pv_accumulate(const float (*pl)[G], int tpv, const uint4 (&vv)[Geom<T, D>::CPL],
@@ -265,8 +288,11 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs &a, int row, 
         wave_lds_sync();
     };
 
+    // The split's block ids, 64 at a time, one per lane: a block's K/V loads take its id with a
+    // lane read (j is uniform) instead of waiting on a table load of their own.
+    TableWindow tw(tab, tab_stride, j0, j1, lane);
     auto load = [&](int j, uint4(&kk)[KS], uint4(&vv)[CPL]) -> bool {
-        const int blk = tab[(size_t)j * tab_stride];
+        const int blk = tw.id(j);
         if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
         const char *kp = kbase + (size_t)blk * blk_bytes;
         const char *vp = vbase + (size_t)blk * blk_bytes;
@@ -411,8 +437,9 @@ __global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_k
     };
 
     const int32_t *tab = a.table + (size_t)row * a.k_sel * a.tab_stride;
+    TableWindow tw(tab, a.tab_stride, j0, j1, lane);
     auto load = [&](int j, uint4(&kk)[CPL], uint4(&vv)[CPL]) -> bool {
-        const int blk = tab[(size_t)j * a.tab_stride];
+        const int blk = tw.id(j);
         if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
         const char *kp = kbase + (size_t)blk * blk_bytes;
         const char *vp = vbase + (size_t)blk * blk_bytes;
