@@ -43,6 +43,10 @@ CASES = {
     "rowstep_ke0": dict(batch=64, n_q_heads=16, n_kv_heads=4, head_dim=128, n_blocks=30, kq=8, ke=0, seed=67),
     "rowstep_long_rows": dict(batch=32, n_q_heads=16, n_kv_heads=8, head_dim=128, n_blocks=1500, kq=8, ke=7,
                               seed=68),
+    # 512 rows keep a single split with a 70-block budget: the attention walks more than one
+    # 64-entry window of block ids
+    "rowstep_wide_budget": dict(batch=128, n_q_heads=16, n_kv_heads=4, head_dim=64, n_blocks=80, kq=40, ke=30,
+                                seed=70),
 }
 
 
