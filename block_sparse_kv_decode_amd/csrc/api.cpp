@@ -4,6 +4,7 @@
 // error paths run (and are tested) on machines without a GPU.
 #include "nosa.h"
 
+#include <float.h>
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -72,18 +73,19 @@ int check_shape(const nosa_shape *s) {
         return fail(NOSA_EUNSUPPORTED, "sub_block_size must be 8, 16, 32 or 64 (got %d)", s->sub_block_size);
     if (s->dtype != NOSA_F32 && s->dtype != NOSA_BF16)
         return fail(NOSA_EUNSUPPORTED, "dtype must be NOSA_F32 or NOSA_BF16 (got %d)", s->dtype);
-    if (s->kq < 0 || s->ke < 0 || s->kq + s->ke < 1)
+    if (s->kq < 0 || s->ke < 0 || (long long)s->kq + s->ke < 1)
         return fail(NOSA_EINVAL, "budget kq=%d ke=%d: both >= 0 and kq + ke >= 1", s->kq, s->ke);
     if (s->n_blocks_max < 1 || s->n_blocks_max > kMaxBlocks)
         return s->n_blocks_max < 1 ? fail(NOSA_EINVAL, "n_blocks_max must be >= 1")
                                    : fail(NOSA_EUNSUPPORTED, "n_blocks_max %d exceeds %d", s->n_blocks_max, kMaxBlocks);
     if (s->n_blocks < 1 || s->n_blocks > s->n_blocks_max)
         return fail(NOSA_EINVAL, "n_blocks %d must lie in [1, n_blocks_max=%d]", s->n_blocks, s->n_blocks_max);
-    if (s->kq + s->ke > s->n_blocks)
-        return fail(NOSA_EINVAL, "budget kq + ke = %d exceeds the %d visible blocks", s->kq + s->ke, s->n_blocks);
+    if ((long long)s->kq + s->ke > s->n_blocks)
+        return fail(NOSA_EINVAL, "budget kq + ke = %lld exceeds the %d visible blocks", (long long)s->kq + s->ke,
+                    s->n_blocks);
     if (s->decode_splits < 0 || s->select_parts < 0)
         return fail(NOSA_EINVAL, "decode_splits and select_parts must be >= 0");
-    if (s->sink_blocks < 0 || s->window_blocks < 0 || s->sink_blocks + s->window_blocks > s->ke)
+    if (s->sink_blocks < 0 || s->window_blocks < 0 || (long long)s->sink_blocks + s->window_blocks > s->ke)
         return fail(NOSA_EINVAL, "sink_blocks (%d) and window_blocks (%d) must be >= 0 and fit in ke (%d)",
                     s->sink_blocks, s->window_blocks, s->ke);
     if (s->n_blocks < s->sink_blocks + s->window_blocks)
@@ -485,7 +487,7 @@ static int check_decode_args(const void *q, const void *k_store, const void *v_s
     REQUIRE_PTR(out, 16);
     REQUIRE_PTR(ws, kAlign);
     if (store_blocks < 1) return fail(NOSA_EINVAL, "store_blocks must be >= 1 (got %d)", store_blocks);
-    if (!(softmax_scale > 0.0f) || softmax_scale != softmax_scale)
+    if (!(softmax_scale > 0.0f) || !(softmax_scale <= FLT_MAX))   // also rejects NaN and +inf
         return fail(NOSA_EINVAL, "softmax_scale must be a positive finite number");
     return NOSA_OK;
 }

@@ -233,8 +233,11 @@ int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_sto
  * score a row in several workgroups and rank Gamma_q in a kernel of its own (rows of more than
  * 64 KiB of pooled keys and fewer than 256 rows; bf16; kq, ke > 0; n_blocks <= 512), the ranking
  * moves into the attention launch instead: the splits over Gamma_e start at once, and each split
- * over Gamma_q ranks the row's Gamma_q itself, so the ranking hides under attention.  Otherwise the
- * step is the two calls.  The workspace is that of nosa_workspace_bytes.
+ * over Gamma_q ranks the row's Gamma_q itself, so the ranking hides under attention.  When one
+ * 256-thread workgroup would both score-and-select a row and attend it in a single split (256 rows
+ * or more and a budget that gives one split per row; bf16), the whole step is one launch: each
+ * workgroup scores, selects and attends its own row.  Otherwise the step is the two calls.  The
+ * workspace is that of nosa_workspace_bytes.
  */
 int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
                      int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, const void *k_store,

@@ -65,6 +65,9 @@ BAD = [
     (dict(sink_blocks=-1), N.NOSA_EINVAL),
     (dict(sink_blocks=1, window_blocks=32), N.NOSA_EINVAL),   # sink + window > ke
     (dict(kq=1, ke=8, window_blocks=8, n_blocks=9, n_blocks_max=9, sink_blocks=1), N.NOSA_EINVAL),
+    (dict(kq=2**31 - 1, ke=1), N.NOSA_EINVAL),                      # kq + ke overflows int32
+    (dict(kq=2**31 - 1, ke=2**31 - 1), N.NOSA_EINVAL),
+    (dict(sink_blocks=2**31 - 1, window_blocks=2**31 - 1), N.NOSA_EINVAL),   # sink + window overflows
 ]
 
 
@@ -93,6 +96,8 @@ def test_invalid_pointers_rejected_on_host():
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 0, 16, 0.1, 16, 256, stream=0),    # store_blocks 0
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, -1.0, 16, 256, stream=0), # bad scale
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, float("nan"), 16, 256, stream=0),
+        lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, 16, float("inf"), 16, 256, stream=0),
+        lambda: N.nosa_decode_step(s, 16, 16, 16, 0, 16, 16, 16, 16, 256, float("inf"), 16, 256, stream=0),
         lambda: N.nosa_sparse_decode(s, 16, 16, 16, 256, None, 0.1, 16, 256, stream=0),
         lambda: N.nosa_pool_keys(s, 16, 250, 10, 16, stream=0),                 # past n_blocks_max
         lambda: N.nosa_pool_keys(s, 16, -1, 1, 16, stream=0),
