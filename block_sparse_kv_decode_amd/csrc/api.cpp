@@ -581,7 +581,8 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
                        shape->n_blocks <= kStepMaxBlocks;
     // One workgroup per row does it all when it would both score-and-select the row and attend it
     // in a single split anyway.
-    const bool row_fused = shape->dtype == NOSA_BF16 && pp.P == 1 && pp.threads == 256 && dp.S == 1;
+    const bool row_fused = shape->dtype == NOSA_BF16 && pp.P == 1 && pp.threads == 256 && dp.S == 1 &&
+                           row_step_fits(shape->n_blocks, shape->kq + shape->ke);
     if (row_fused) {
         SelectArgs sa;
         if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, stream,

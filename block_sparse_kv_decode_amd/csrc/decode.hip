@@ -195,20 +195,63 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, int row, int s
 }  // namespace
 
 // ---- bf16: QK on the matrix cores -----------------------------------------------------------
+// Where this lane's K and V chunks of a block lie: wave w covers tokens [16w, 16w + 16); K in the
+// MFMA A layout (lane = key row j16 of k-group grp), V as contiguous 1 KiB lines (PV layout).
+template <int D>
+struct BlockAddr {
+    using Gm = Geom<uint16_t, D>;
+    static constexpr int KS = D / 32, CPL = Gm::CPL, RB = Gm::RB;
+    const char *kbase, *vbase;
+    int kofs[KS], vofs[CPL];
+    __device__ __forceinline__ BlockAddr(const DecodeArgs &a, int row) {
+        const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+        const int j16 = lane & 15, grp = lane >> 4;
+        const int cpv = lane % Gm::NC, tpv = lane / Gm::NC;
+        const size_t rowb = (size_t)row * a.store_blocks * blk_bytes() + (size_t)w * kTokPerWave * RB;
+        kbase = (const char *)a.k + rowb;
+        vbase = (const char *)a.v + rowb;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kofs[ks] = j16 * RB + (4 * ks + grp) * 16;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) vofs[i] = (i * Gm::TPI + tpv) * RB + cpv * 16;
+    }
+    static constexpr size_t blk_bytes() { return (size_t)kBlockTokens * RB; }
+    // Issues the loads of block blk (false, and no loads, for an id outside the store).
+    __device__ __forceinline__ bool issue(const DecodeArgs &a, int blk, uint4 (&kk)[KS], uint4 (&vv)[CPL]) const {
+        if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
+        const char *kp = kbase + (size_t)blk * blk_bytes();
+        const char *vp = vbase + (size_t)blk * blk_bytes();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kk[ks] = *(const uint4 *)(kp + kofs[ks]);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) vv[i] = *(const uint4 *)(vp + vofs[i]);
+        return true;
+    }
+};
+
+// Two blocks whose loads a caller issued ahead of the split (the split's first two entries).
+template <int D>
+struct PreBlocks {
+    uint4 k0[D / 32], v0[D / 32], k1[D / 32], v1[D / 32];
+    bool o0 = false, o1 = false;
+};
+
 // One split: entries [j0, j1) of the row's table (tab[j * tab_stride], block ids into the store),
-// written as partial slot sp of the row (or the output itself when a.direct).
-template <int D, int G>
+// written as partial slot sp of the row (or the output itself when a.direct).  With PRE, the loads
+// of entries j0 and j0 + 1 were already issued into *pre.
+template <int D, int G, bool PRE = false>
 __device__ __forceinline__ void decode_mfma_split(const DecodeArgs &a, int row, int sp, const int32_t *tab,
-                                                  int tab_stride, int j0, int j1, SplitShared<D, G> &sh) {
+                                                  int tab_stride, int j0, int j1, SplitShared<D, G> &sh,
+                                                  PreBlocks<D> *pre = nullptr) {
     using Gm = Geom<uint16_t, D>;
     constexpr int KS = D / 32;                        // 32-dim MFMA steps
-    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB, TPI = Gm::TPI;
+    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB;
     static_assert(CPL == KS, "bf16 rows: one V chunk per MFMA step");
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int j16 = lane & 15, grp = lane >> 4;       // MFMA layout: column (head) / k-group
-    const int cpv = lane % NC, tpv = lane / NC;       // PV layout
+    const int tpv = lane / NC;                        // PV layout
 
     // B operand: q of head j16 (zero columns beyond G), dims 32 ks + 8 grp .. + 8
     bf16x8_t qb[KS];
@@ -222,14 +265,7 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs &a, int row, 
         }
     }
 
-    const size_t blk_bytes = (size_t)kBlockTokens * RB;
-    const char *kbase = (const char *)a.k + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
-    const char *vbase = (const char *)a.v + (size_t)row * a.store_blocks * blk_bytes + (size_t)w * kTokPerWave * RB;
-    int kofs[KS], vofs[CPL];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kofs[ks] = j16 * RB + (4 * ks + grp) * 16;   // A operand: key row j16
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) vofs[i] = (i * TPI + tpv) * RB + cpv * 16;
+    const BlockAddr<D> ba(a, row);
 
     float m = -INFINITY;          // running max of head j16 (lanes j16 < G)
     float lq = 0.0f;              // running sum of p over this lane's 4 tokens of head j16
@@ -291,23 +327,26 @@ __device__ __forceinline__ void decode_mfma_split(const DecodeArgs &a, int row, 
     // The split's block ids, 64 at a time, one per lane: a block's K/V loads take its id with a
     // lane read (j is uniform) instead of waiting on a table load of their own.
     TableWindow tw(tab, tab_stride, j0, j1, lane);
-    auto load = [&](int j, uint4(&kk)[KS], uint4(&vv)[CPL]) -> bool {
-        const int blk = tw.id(j);
-        if ((unsigned)blk >= (unsigned)a.store_blocks) return false;
-        const char *kp = kbase + (size_t)blk * blk_bytes;
-        const char *vp = vbase + (size_t)blk * blk_bytes;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kk[ks] = *(const uint4 *)(kp + kofs[ks]);
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) vv[i] = *(const uint4 *)(vp + vofs[i]);
-        return true;
-    };
+    auto load = [&](int j, uint4(&kk)[KS], uint4(&vv)[CPL]) -> bool { return ba.issue(a, tw.id(j), kk, vv); };
 
     // three register buffers: blocks j+1 and j+2 are in flight while block j is computed
     uint4 kb0[KS], vb0[CPL], kb1[KS], vb1[CPL], kb2[KS], vb2[CPL];
     int j = j0;
-    bool o0 = (j < j1) ? load(j, kb0, vb0) : false;
-    bool o1 = (j + 1 < j1) ? load(j + 1, kb1, vb1) : false;
+    bool o0, o1;
+    if (PRE) {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            kb0[i] = pre->k0[i];
+            vb0[i] = pre->v0[i];
+            kb1[i] = pre->k1[i];
+            vb1[i] = pre->v1[i];
+        }
+        o0 = pre->o0;
+        o1 = pre->o1;
+    } else {
+        o0 = (j < j1) ? load(j, kb0, vb0) : false;
+        o1 = (j + 1 < j1) ? load(j + 1, kb1, vb1) : false;
+    }
     bool o2 = false;
     while (j < j1) {
         if (j + 2 < j1) o2 = load(j + 2, kb2, vb2);
@@ -545,17 +584,38 @@ __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectAr
     __shared__ SplitShared<D, G> sh;
     __shared__ SelectShared<256> ssh;
     const int row = blockIdx.x;
-    const RowLds L = carve<256>(dyn, s.n_blocks);
+    const int n = s.n_blocks, k = s.kq + s.ke;
+    const RowLds L = carve<256>(dyn, n);
+    int32_t *wl = (int32_t *)(dyn + row_lds_bytes<256>(n));   // [k]: Gamma_e, then Gamma_q, each ascending
     float e[kEvPre];
     ev_load<256>(s, row, e);
-    score_range<uint16_t, D, SPB, 256>(s, row, 0, s.n_blocks, L.sc, nullptr);
-    ev_store<256>(s, row, L, s.n_blocks, e);
-    __syncthreads();
+    score_range<uint16_t, D, SPB, 256>(s, row, 0, n, L.sc, nullptr);
+    ev_store<256>(s, row, L, n, e);
+    wg_barrier();
     select_agnostic<256>(s, row, L, ssh);
+    compact_outputs<256>(n, L.inE, L.inE, wl, s.ke, nullptr, 0, ssh);
+    wg_barrier();
+    // The first two Gamma_e blocks' loads go out now and stay in flight through the Gamma_q
+    // ranking, whose barriers wait for LDS only.  (Not at d 128 with 8 query heads per KV head:
+    // holding the two blocks through the ranking would spill registers.)
+    constexpr bool kPre = !(D == 128 && G == 8);
+    PreBlocks<D> pre;
+    if (kPre && s.ke >= 2) {
+        const BlockAddr<D> ba(a, row);
+        pre.o0 = ba.issue(a, wl[0], pre.k0, pre.v0);
+        pre.o1 = ba.issue(a, wl[1], pre.k1, pre.v1);
+    }
     select_query<256>(s, row, L, ssh, true);
-    __syncthreads();   // this workgroup's selection, written to global memory, is visible to it
-    const int k = s.kq + s.ke;
-    decode_mfma_split<D, G>(a, row, 0, s.sel + (size_t)row * k, 1, 0, k, sh);
+    compact_outputs<256>(n, L.inQ, L.inQ, wl + s.ke, s.kq, nullptr, 0, ssh);
+    wg_barrier();
+    if (kPre && s.ke >= 2)
+        decode_mfma_split<D, G, kPre>(a, row, 0, wl, 1, 0, k, sh, &pre);
+    else
+        decode_mfma_split<D, G>(a, row, 0, wl, 1, 0, k, sh);
+}
+
+bool row_step_fits(int n_blocks, int k) {
+    return row_lds_bytes<256>(n_blocks) + 4 * (size_t)k <= kRowStepMaxLds;
 }
 
 // Merges the St split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
@@ -638,7 +698,7 @@ hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArg
 
 template <int D, int G, int SPB>
 static hipError_t launch_row_step_t(const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st) {
-    const size_t dyn = row_lds_bytes<256>(s.n_blocks);
+    const size_t dyn = row_lds_bytes<256>(s.n_blocks) + 4 * (size_t)(s.kq + s.ke);
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)row_step_kernel<D, G, SPB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);

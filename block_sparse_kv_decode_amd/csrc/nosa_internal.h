@@ -118,5 +118,9 @@ hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArg
 // bf16 decode step in one workgroup per row: scoring, selection and single-split attention.
 hipError_t launch_row_step(int d, int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
                            hipStream_t st);
+// Dynamic LDS of the one-workgroup-per-row step (the row's selection state plus its k-entry work
+// list) within this bound, which leaves room for two workgroups per CU in the 160 KiB of LDS.
+constexpr size_t kRowStepMaxLds = 56 * 1024;
+bool row_step_fits(int n_blocks, int k);
 
 }  // namespace nosa

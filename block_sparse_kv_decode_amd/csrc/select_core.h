@@ -18,6 +18,15 @@ constexpr int kEvPre = 4;            // eviction scores prefetched per thread
 constexpr int kEvLdsMax = 4096;      // rows up to this length keep their eviction scores in LDS
 constexpr int kKeyScratch = 256 + kCandMax;   // uint64 LDS entries of the top-k scratch
 
+// Workgroup barrier for LDS: waits for this wave's LDS accesses only, so global loads a caller
+// left in flight (prefetched K/V blocks) stay in flight.  The selection helpers read global
+// memory only as input and write it only as output, so LDS is all their barriers must order.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int NT>
 struct SelectShared {
     uint32_t hist[256];
@@ -36,7 +45,7 @@ __device__ __forceinline__ int block_incl_scan(int v, int *ws) {
         if (lane >= o) v += t;
     }
     if (lane == 63) ws[w] = v;
-    __syncthreads();
+    wg_barrier();
     if (NW > 1 && w == 0) {
         int t = lane < NW ? ws[lane] : 0;
 #pragma unroll
@@ -46,9 +55,9 @@ __device__ __forceinline__ int block_incl_scan(int v, int *ws) {
         }
         if (lane < NW) ws[lane] = t;   // inclusive prefix of the wave totals
     }
-    __syncthreads();
+    wg_barrier();
     const int add = w > 0 ? ws[w - 1] : 0;
-    __syncthreads();
+    wg_barrier();
     return v + add;
 }
 
@@ -66,23 +75,23 @@ __device__ void topk_radix(int n, int kk, KeyF key, CandF cand, uint8_t *mark, S
         const int shift = 24 - 8 * pass;
         if (tid < 256) sh.hist[tid] = 0u;
         if (tid == 0) { sh.bcast[0] = 0; sh.bcast[1] = 0; }
-        __syncthreads();
+        wg_barrier();
         for (int i = tid; i < n; i += NT) {
             if (cand(i)) {
                 const uint32_t kv = key(i);
                 if ((kv & pmask) == prefix) atomicAdd(&sh.hist[(kv >> shift) & 255u], 1u);
             }
         }
-        __syncthreads();
+        wg_barrier();
         const int cnt = tid < 256 ? (int)sh.hist[255 - tid] : 0;
         const int ge = block_incl_scan<NT>(cnt, sh.scan);   // candidates with digit >= 255 - tid
         const int gt = ge - cnt;
         if (tid < 256 && gt < need && need <= ge) { sh.bcast[0] = 255 - tid; sh.bcast[1] = gt; }
-        __syncthreads();
+        wg_barrier();
         prefix |= (uint32_t)sh.bcast[0] << shift;
         pmask |= 0xFFu << shift;
         need -= sh.bcast[1];
-        __syncthreads();
+        wg_barrier();
     }
     // prefix is the kk-th largest key; take every larger key and the `need` lowest ids equal to it.
     const uint32_t T = prefix;
@@ -102,7 +111,7 @@ __device__ void topk_radix(int n, int kk, KeyF key, CandF cand, uint8_t *mark, S
             ++rank;
         }
     }
-    __syncthreads();
+    wg_barrier();
 }
 
 // Marks the kk largest of the m unique keys buf[0..m) (zeros are empty slots): several lanes of a
@@ -161,9 +170,9 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
     const int tid = threadIdx.x;
     if (n <= kRankMaxBlocks) {
         for (int i = tid; i < n; i += NT) keybuf[i] = cand(i) ? composite_key(key(i), i) : 0ull;
-        __syncthreads();
+        wg_barrier();
         rank_mark<NT>(keybuf, n, kk, [&](int i, uint64_t, int) { mark[i] = 1; });
-        __syncthreads();
+        wg_barrier();
         return;
     }
     constexpr int kChunks = 256;
@@ -188,14 +197,14 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
         if (part == 0) tmax[ch] = best;
         if (tid == 0) cbuf[0] = 1ull;   // T0 when fewer than kk chunks hold a candidate: keep all
     }
-    __syncthreads();
+    wg_barrier();
     // threshold T0: the kk-th best chunk maximum (the maximum ranked kk - 1)
     rank_mark<NT>(tmax, kChunks, kk, [&](int, uint64_t ki, int rank) {
         if (rank == kk - 1) cbuf[0] = ki;
     });
-    __syncthreads();
+    wg_barrier();
     const uint64_t T0 = cbuf[0];
-    __syncthreads();
+    wg_barrier();
     const int per = (n + NT - 1) / NT;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int cnt = 0;
@@ -203,7 +212,7 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
         if (cand(i) && composite_key(key(i), i) >= T0) ++cnt;
     const int incl = block_incl_scan<NT>(cnt, sh.scan);
     if (tid == NT - 1) sh.bcast[2] = incl;
-    __syncthreads();
+    wg_barrier();
     const int total = sh.bcast[2];
     if (total <= kCandMax) {
         int pos = incl - cnt;
@@ -212,9 +221,9 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
                 const uint64_t c = composite_key(key(i), i);
                 if (c >= T0) cbuf[pos++] = c;
             }
-        __syncthreads();
+        wg_barrier();
         rank_mark<NT>(cbuf, total, kk, [&](int, uint64_t c, int) { mark[0xFFFFFFFFu - (uint32_t)c] = 1; });
-        __syncthreads();
+        wg_barrier();
         return;
     }
     topk_radix<NT>(n, kk, key, cand, mark, sh);
@@ -243,7 +252,7 @@ __device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, i
         }
     }
     if (tid == NT - 1) sh.bcast[2] = incl;
-    __syncthreads();
+    wg_barrier();
     const int ns = sh.bcast[2] & 0xFFFF, ne = sh.bcast[2] >> 16;
     if (sel)
         for (int p = ns + tid; p < k; p += NT) sel[p] = -1;
@@ -327,7 +336,7 @@ __device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, S
         L.inE[i] = 0;
         L.inQ[i] = 0;
     }
-    __syncthreads();
+    wg_barrier();
     const int n_prev = a.n_prev;
     const bool fresh = (n_prev == 0);
     const int w_lo = n - a.n_window;              // first window block
@@ -339,7 +348,7 @@ __device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, S
         }
     for (int i = tid; i < n; i += NT)
         if (i < a.n_sink || i >= w_lo) L.inE[i] = 1;
-    __syncthreads();
+    wg_barrier();
     const float *evg = a.ev + (size_t)row * a.n_blocks_max;
     const float *evl = L.ev;
     const uint8_t *prevE = L.inQ;
@@ -348,7 +357,7 @@ __device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, S
         n, a.ke - a.n_sink - a.n_window, [&](int i) { return order_key(evl ? evl[i] : evg[i]); },
         [&](int i) { return i >= n_sink && i < w_lo && (fresh || i >= left || prevE[i]); }, L.inE, L.keys, sh);
     for (int i = tid; i < n; i += NT) L.inQ[i] = 0;
-    __syncthreads();
+    wg_barrier();
 }
 
 // Gamma_q of one row from the block scores in L.sc and Gamma_e in L.inE, then the outputs in
