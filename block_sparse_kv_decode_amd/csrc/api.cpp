@@ -43,7 +43,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Rows (batch x KV heads) per call: keeps every grid (rows x splits or parts) within 2^31 workgroups.
 constexpr int kMaxRows = 1 << 16;
 // Work distribution targets: enough workgroups to give every one of the 256 CUs two of them.
-constexpr int kTargetWorkgroups = 512;
+constexpr int kCUs = 256;
+constexpr int kTargetWorkgroups = 2 * kCUs;
 constexpr int kMinBlocksPerPart = 8;
 // A split shorter than this many blocks spends more time filling its load pipeline and merging
 // than it saves (measured on MI355X: 4-block splits lose to 8-block splits at 128K context).
@@ -139,9 +140,16 @@ PartPlan select_plan(const nosa_shape *s) {
         const size_t row_bytes = (size_t)n * spb_of(s) * s->head_dim * sizeof(float);
         if (threads == 256 || row_bytes <= kFusedRowBytes) {
             P = 1;
+        } else if (part_threads == 1024) {
+            // A 1024-thread workgroup fills a CU, so the parts and the row's Gamma_e workgroup
+            // together take one CU each: all of them start at once.  (Measured on MI355X at 2048
+            // blocks per row and 32 rows: 7 parts 47.5 us per step, 4 parts 49.5 us, and 8 parts,
+            // whose last workgroups wait for a free CU, 50.8 us.)
+            P = kCUs / R - 1;
+            const int cap = n / kMinBlocksPerPart > 0 ? n / kMinBlocksPerPart : 1;
+            if (P > cap) P = cap;
         } else {
-            const int target = kTargetWorkgroups * 256 / part_threads;
-            P = (target + R - 1) / R;
+            P = (kTargetWorkgroups + R - 1) / R;
             const int cap = n / kMinBlocksPerPart > 0 ? n / kMinBlocksPerPart : 1;
             if (P > cap) P = cap;
         }
