@@ -159,10 +159,12 @@ __device__ __forceinline__ void rank_mark(const uint64_t *buf, int m, int kk, Ma
 // Marks the kk best candidates (key descending, id ascending) in mark[0..n).  Keys are made
 // unique by appending the inverted block id (composite_key), so the kk-th best is well defined.
 //   n <= 512 : every candidate is ranked against all others (rank_mark).
-//   n  > 512 : the row is cut into 256 chunks; the kk-th best chunk maximum is a lower bound T0 of
-//              the kk-th best key overall (the kk best maxima are distinct keys >= T0), and at
-//              most kk chunks hold keys >= T0, so at most kk * chunk candidates survive; they are
-//              gathered and ranked.  When more than kCandMax survive, a radix select takes over.
+//   n  > 512 : the row is cut into at most 256 chunks; the kk-th best chunk maximum is a lower bound
+//              T0 of the kk-th best key overall (the kk best maxima are distinct keys >= T0), and
+//              at most kk chunks hold keys >= T0, so at most kk * chunk candidates survive; they
+//              are gathered (in any order: the ranking needs none) and ranked.  Chunks are as long
+//              as kCandMax / kk allows, so that few maxima are ranked.  When more than kCandMax
+//              survive, a radix select takes over.
 // keybuf: LDS scratch of 256 + kCandMax uint64.
 template <int NT, class KeyF, class CandF>
 __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, uint64_t *keybuf, SelectShared<NT> &sh) {
@@ -175,11 +177,13 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
         wg_barrier();
         return;
     }
-    constexpr int kChunks = 256;
-    constexpr int TPCH = NT / kChunks;              // threads per chunk (adjacent lanes)
-    uint64_t *tmax = keybuf;                        // [256] chunk maxima
-    uint64_t *cbuf = keybuf + kChunks;              // [kCandMax] surviving candidates
-    const int csize = (n + kChunks - 1) / kChunks;
+    constexpr int kMaxChunks = 256;
+    constexpr int TPCH = NT / kMaxChunks;           // threads per chunk (adjacent lanes)
+    uint64_t *tmax = keybuf;                        // [nch] chunk maxima
+    uint64_t *cbuf = keybuf + kMaxChunks;           // [kCandMax] surviving candidates
+    int csize = kCandMax / kk;                      // at most kk * csize keys survive
+    if (csize < (n + kMaxChunks - 1) / kMaxChunks) csize = (n + kMaxChunks - 1) / kMaxChunks;
+    const int nch = (n + csize - 1) / csize;        // <= 256
     {
         const int ch = tid / TPCH, part = tid - ch * TPCH;
         const int lo = min(n, ch * csize), hi = min(n, lo + csize);
@@ -194,28 +198,28 @@ __device__ void topk_mark(int n, int kk, KeyF key, CandF cand, uint8_t *mark, ui
                                    (uint32_t)__shfl_xor((int)(uint32_t)best, o, 64);
             best = other > best ? other : best;
         }
-        if (part == 0) tmax[ch] = best;
+        if (part == 0 && ch < nch) tmax[ch] = best;
         if (tid == 0) cbuf[0] = 1ull;   // T0 when fewer than kk chunks hold a candidate: keep all
     }
     wg_barrier();
     // threshold T0: the kk-th best chunk maximum (the maximum ranked kk - 1)
-    rank_mark<NT>(tmax, kChunks, kk, [&](int, uint64_t ki, int rank) {
+    rank_mark<NT>(tmax, nch, kk, [&](int, uint64_t ki, int rank) {
         if (rank == kk - 1) cbuf[0] = ki;
     });
     wg_barrier();
     const uint64_t T0 = cbuf[0];
+    if (tid == 0) sh.bcast[3] = 0;
     wg_barrier();
     const int per = (n + NT - 1) / NT;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int cnt = 0;
     for (int i = lo; i < hi; ++i)
         if (cand(i) && composite_key(key(i), i) >= T0) ++cnt;
-    const int incl = block_incl_scan<NT>(cnt, sh.scan);
-    if (tid == NT - 1) sh.bcast[2] = incl;
+    const int pos0 = cnt ? atomicAdd(&sh.bcast[3], cnt) : 0;   // a slot range of cbuf per thread
     wg_barrier();
-    const int total = sh.bcast[2];
+    const int total = sh.bcast[3];
     if (total <= kCandMax) {
-        int pos = incl - cnt;
+        int pos = pos0;
         for (int i = lo; i < hi; ++i)
             if (cand(i)) {
                 const uint64_t c = composite_key(key(i), i);
