@@ -131,3 +131,33 @@ def test_decode_step_multistep_with_arrivals(plan):
         _, agn_ref, _ = O.select(s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref)
         agn = agn_new
         qf = f32_to_bf16_bits((H.as_f64(qf) + 0.3 * rng.standard_normal(qf.shape)).astype(np.float32))
+
+
+EVERY_BLOCK = {
+    # one workgroup per row (512 rows, one split), the pick inside attention (rows above 64 KiB of
+    # pooled keys), and the two calls (short rows)
+    "rowstep": dict(batch=128, n_q_heads=16, n_kv_heads=4, head_dim=64, n_blocks=12, kq=5, ke=7, seed=71),
+    "fused": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=150, kq=90, ke=60, seed=72),
+    "two_calls": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=30, kq=10, ke=20, seed=73),
+}
+
+
+@pytest.mark.parametrize("plan", sorted(EVERY_BLOCK))
+def test_decode_step_selects_every_block(plan):
+    # A budget equal to the visible blocks selects all of them: the selection is 0..n-1 in every row,
+    # and sparse attention is dense decode attention over the whole context.
+    w = small_workload("every_" + plan, **EVERY_BLOCK[plan])
+    assert w.k == w.n_blocks
+    x = generate(w)
+    shape = H.shape_of(w)
+    q, k, v, ev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
+    kp = H.gpu_pool(shape, k)
+    ws = N.workspace(shape)
+    agn0 = torch.full((w.rows, w.ke), -7, dtype=torch.int32, device="cuda")
+    sel, agn, out = _step(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    assert (H.host(sel) == np.arange(w.n_blocks, dtype=np.int32)).all()
+    s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], 32), w.n_blocks, 2)
+    H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke)
+    every = np.broadcast_to(np.arange(w.n_blocks, dtype=np.int32), (w.batch, w.n_kv_heads, w.n_blocks)).copy()
+    ref = O.attention(x["q"], x["k"], x["v"], every)
+    H.check_attention(H.host(out), ref, "bf16", "every block (%s)" % plan)
