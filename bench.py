@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -41,9 +42,13 @@ KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_kv_decode_amd", "csrc", f)
 
 
 def kernel_src_sha256():
+    """SHA-256 of the kernel sources' code: comments and blank space are dropped first, so an edit
+    to a comment does not void counter records taken on the same code."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+        text = re.sub(r"/\*.*?\*/", " ", open(f).read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip()).encode())
     return h.hexdigest()
 
 

@@ -23,7 +23,8 @@
 //              V would need a transpose to feed the matrix cores).  Probabilities travel through
 //              16 x G floats of LDS.
 //   Prefetch : K and V of the next blocks are loaded into registers while a block is computed
-//              (two blocks ahead for bf16, one for fp32).
+//              (two blocks ahead for bf16, one for fp32).  A split reads its block ids once, 64
+//              to a register (one per lane), so no block's loads wait on a table read.
 // End of split: lane reduction, a 4-wave merge through LDS, then either the final output
 // (one split) or a (max, sum, acc) partial in the workspace, merged by combine_kernel with the same
 // online-softmax rule.  No workgroup waits on another.  A launch may fill only some of a row's
@@ -577,7 +578,8 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
 // Grid rows, bf16, for plans where one 256-thread workgroup scores and selects a row and a single
 // split attends it (many rows, short rows): the workgroup scores its row, selects (writing
 // agn_state and the selection), and attends the selected blocks straight after, so each row's
-// attention starts when its own selection is done rather than when the slowest row's is.
+// attention starts when its own selection is done rather than when the slowest row's is.  The
+// loads of the first two Gamma_e blocks go out before the Gamma_q ranking and land during it.
 template <int D, int G, int SPB>
 __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectArgs s) {
     extern __shared__ __align__(16) unsigned char dyn[];
