@@ -51,7 +51,8 @@ constexpr int kMinBlocksPerPart = 8;
 constexpr int kMinBlocksPerSplit = 8;
 // Rows up to this many blocks run the fused decode step: their Gamma_q ranking in a 256-thread
 // workgroup is a single pass.  Longer rows rank more slowly there than the attention splits can
-// hide (measured on MI355X at 2048 blocks per row: 48.7 us per step fused vs 44.2 us in two calls).
+// hide (measured on MI355X at 2048 blocks per row and 32 rows: 49.4 us per step fused vs 46.2 us
+// in two calls).
 constexpr int kStepMaxBlocks = 512;
 
 int check_shape(const nosa_shape *s) {

@@ -22,13 +22,15 @@
 //   Exact top-k on unique 64-bit keys (order-preserving score bits, then the inverted block id,
 //   so equal scores go to the lower id): rows of up to 512 blocks rank every candidate against
 //   all others, several lanes sharing each count; longer rows first drop every key below a bound
-//   taken from 256 chunk maxima and rank the survivors (radix select as the fallback).  Outputs
-//   are compacted in ascending block id.
+//   taken from the maxima of at most 256 chunks and rank the survivors (radix select as the
+//   fallback).  Outputs are compacted in ascending block id.  The selection's workgroup barriers
+//   wait for LDS only.
 // Launch plans (chosen on the host).  "fused": one workgroup (256 or 1024 threads) scores a
-//   whole row and selects from LDS.  "parts": several 256-thread workgroups score slices of a
-//   row into the workspace while one more workgroup per row picks Gamma_e from the eviction
-//   scores; a second kernel (1024 threads per row) picks Gamma_q.  No workgroup ever waits on
-//   another inside a kernel.
+//   whole row and selects from LDS.  "parts": several workgroups (256 threads, or 1024 for rows
+//   over 1024 blocks) score slices of a row into the workspace while one more workgroup per row
+//   picks Gamma_e from the eviction scores; a second kernel (1024 threads per row) picks Gamma_q,
+//   unless the one-call decode step ranks it inside its attention launch.  No workgroup ever
+//   waits on another inside a kernel.
 #include "select_core.h"
 
 namespace nosa {
