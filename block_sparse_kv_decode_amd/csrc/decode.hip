@@ -621,25 +621,48 @@ bool row_step_fits(int n_blocks, int k) {
 }
 
 // Merges the St split partials (max, sum, acc) of one (row, head) into the output; thread = dim.
-// Empty partials (max = -inf) carry nothing and are passed over.
+// Empty partials (max = -inf) carry nothing and are passed over.  The partials are read kChunk
+// splits at a time, every load issued before any is used (one memory round trip per chunk rather
+// than two per split); each chunk is folded in against the largest max seen so far.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
+    constexpr int kChunk = 8;
     const int row = blockIdx.x / G, h = blockIdx.x - row * G;
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int dd = threadIdx.x;
     const float *rp = a.part + ((size_t)row * a.St * G + h) * (D + 2);
     const size_t stride = (size_t)G * (D + 2);
     float M = -INFINITY, L = 0.0f, A = 0.0f;
-#pragma unroll 4
-    for (int s = 0; s < a.St; ++s) {
-        const float *ps = rp + s * stride;
-        const float ms = ps[0], ls = ps[1], as = ps[2 + dd];   // loaded together, tested after
-        if (ms == -INFINITY) continue;
-        const float mn = fmaxf(M, ms);
-        const float fo = fast_exp2(M - mn), fn = fast_exp2(ms - mn);
-        L = L * fo + ls * fn;
-        A = A * fo + as * fn;
-        M = mn;
+    for (int s0 = 0; s0 < a.St; s0 += kChunk) {
+        float hd[kChunk], as[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            // slots past St re-read the last slot (no branch between the loads) and count as empty;
+            // even lanes load the slot's max, odd lanes its sum (vector loads, waited for in order)
+            const float *ps = rp + (size_t)min(s0 + u, a.St - 1) * stride;
+            hd[u] = ps[dd & 1];
+            as[u] = ps[2 + dd];
+        }
+        float ms[kChunk], ls[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            ms[u] = s0 + u < a.St ? readlane_f(hd[u], 0) : -INFINITY;
+            ls[u] = readlane_f(hd[u], 1);
+        }
+        float mc = M;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, ms[u]);
+        const float fo = M == -INFINITY ? 0.0f : fast_exp2(M - mc);   // L = A = 0 while M is -inf
+        L *= fo;
+        A *= fo;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const bool live = ms[u] != -INFINITY;
+            const float f = fast_exp2(ms[u] - mc);
+            L = live ? fmaf(ls[u], f, L) : L;
+            A = live ? fmaf(as[u], f, A) : A;
+        }
+        M = mc;
     }
     store_elem<T>(a.out, (size_t)(b * a.Hq + g * G + h) * D + dd, A / L);
 }

@@ -88,17 +88,22 @@ template <int NT>
 __global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ SelectShared<NT> sh;
-    const int row = blockIdx.x;
+    const int row = blockIdx.x, tid = threadIdx.x;
     const RowLds L = carve<NT>(dyn, a.n_blocks);
     const float *gscore = a.scores + (size_t)row * a.scores_stride;
-    for (int i = threadIdx.x; i < a.n_blocks; i += NT) {
+    const int32_t *agn = a.agn + (size_t)row * a.ke;
+    // the first NT Gamma_e ids are loaded together with the scores (one memory round trip) and
+    // marked after the clear; any further ids are read after the barrier
+    const int id0 = tid < a.ke ? agn[tid] : -1;
+    for (int i = tid; i < a.n_blocks; i += NT) {
         L.sc[i] = gscore[i];
         L.inE[i] = 0;
         L.inQ[i] = 0;
     }
     __syncthreads();
-    for (int j = threadIdx.x; j < a.ke; j += NT) {
-        const int id = a.agn[(size_t)row * a.ke + j];
+    if (id0 >= 0 && id0 < a.n_blocks) L.inE[id0] = 1;
+    for (int j = tid + NT; j < a.ke; j += NT) {
+        const int id = agn[j];
         if (id >= 0 && id < a.n_blocks) L.inE[id] = 1;
     }
     __syncthreads();
