@@ -48,6 +48,10 @@ __global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
     score_range<T, D, SPB, NT>(a, row, 0, a.n_blocks, L.sc, nullptr);
     ev_store<NT>(a, row, L, a.n_blocks, e);
     __syncthreads();
+    if (a.n_blocks <= kWaveRowMax) {   // a short row: one block per lane, ranked in registers
+        select_row64<NT>(a, row, L, nullptr);
+        return;
+    }
     select_agnostic<NT>(a, row, L, sh);
     select_query<NT>(a, row, L, sh, true);
 }

@@ -379,6 +379,94 @@ __device__ void select_query(const SelectArgs &a, int row, const RowLds &L, Sele
 }
 
 
+// Rows of at most 64 blocks: lane i of every wave holds block i.
+constexpr int kWaveRowMax = 64;
+
+// Rank of lane i's key among the 64 lanes' keys (the number of larger keys), counted by all
+// NT / 64 waves of the workgroup: wave w compares against lanes [w * 64 / NW, (w + 1) * 64 / NW)
+// with lane reads and the partial counts are added through part[NW][64] in LDS.  Every thread
+// calls it with its wave's copy of the keys.
+template <int NT>
+__device__ __forceinline__ int group_rank64(uint64_t key, int *part) {
+    constexpr int NW = NT / 64, JW = 64 / NW;
+    const int i = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < JW; ++u) {
+        const int j = w * JW + u;
+        const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, j) << 32) |
+                            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo, j);
+        cnt += kj > key ? 1 : 0;
+    }
+    if (NW == 1) return cnt;
+    part[w * 64 + i] = cnt;
+    wg_barrier();
+    int r = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) r += part[v * 64 + i];
+    wg_barrier();   // part is written again by the next call
+    return r;
+}
+
+// The whole selection of a row of n <= 64 blocks, with lane i of every wave on block i: Gamma_e
+// (sink and window blocks, plus the best blocks by eviction score among the same candidates as
+// select_agnostic), then Gamma_q (the best block scores outside Gamma_e), both by exact rank of
+// the same unique keys topk_mark uses, so the result is identical.  Wave 0 writes agn_state and
+// the selection like select_query and, when wl is given, Gamma_e then Gamma_q (each ascending,
+// padded with -1 to ke and kq entries) to wl[0..k).  Reads L.sc and L.ev and uses L.keys as
+// scratch; called by all NT threads after the barrier that follows the scoring.
+template <int NT>
+__device__ void select_row64(const SelectArgs &a, int row, const RowLds &L, int32_t *wl) {
+    const int i = threadIdx.x & 63;
+    const int n = a.n_blocks, ke = a.ke, kq = a.kq, k = kq + ke;
+    const bool in_row = i < n;
+    int *part = (int *)L.keys;
+    // previous Gamma_e as a lane mask (strict eviction): ids < n_prev only
+    const int n_prev = a.n_prev;
+    const bool fresh = (n_prev == 0);
+    uint64_t prev = 0ull;
+    if (!fresh && ke > 0) {
+        const int id = i < ke ? a.agn[(size_t)row * ke + i] : -1;
+        const uint64_t has = __ballot(id >= 0 && id < n_prev);
+        for (uint64_t m = has; m; m &= m - 1) {
+            const int j = __builtin_ctzll(m);
+            prev |= 1ull << __builtin_amdgcn_readlane(id, j);
+        }
+    }
+    const int w_lo = n - a.n_window, left = n_prev - a.n_window;
+    const bool forced = in_row && (i < a.n_sink || i >= w_lo);
+    const bool cand_e = in_row && i >= a.n_sink && i < w_lo && (fresh || i >= left || ((prev >> i) & 1ull));
+    const float evi = in_row ? (L.ev ? L.ev[i] : a.ev[(size_t)row * a.n_blocks_max + i]) : 0.0f;
+    const int kk_e = ke - a.n_sink - a.n_window;
+    const int re = group_rank64<NT>(cand_e ? composite_key(order_key(evi), i) : 0ull, part);
+    const bool inE = forced || (cand_e && re < kk_e);
+    const bool cand_q = in_row && !inE;
+    const int rq = group_rank64<NT>(cand_q ? composite_key(order_key(L.sc[i]), i) : 0ull, part);
+    const bool inQ = cand_q && rq < kq;
+    if (threadIdx.x >= 64) return;
+    // outputs in ascending block id
+    const uint64_t mE = __ballot(inE), mQ = __ballot(inQ), mS = mE | mQ;
+    const int pe = lanes_below(mE), pq = lanes_below(mQ), ps = lanes_below(mS);
+    const int ne = __popcll(mE), nq = __popcll(mQ), ns = __popcll(mS);
+    int32_t *agn = a.agn + (size_t)row * ke;
+    int32_t *sel = a.sel + (size_t)row * k;
+    if (inE && pe < ke) {
+        agn[pe] = i;
+        if (wl) wl[pe] = i;
+    }
+    if (inQ && pq < kq && wl) wl[ke + pq] = i;
+    if ((inE || inQ) && ps < k) sel[ps] = i;
+    for (int p = ne + i; p < ke; p += 64) {
+        agn[p] = -1;
+        if (wl) wl[p] = -1;
+    }
+    if (wl)
+        for (int p = nq + i; p < kq; p += 64) wl[ke + p] = -1;
+    for (int p = ns + i; p < k; p += 64) sel[p] = -1;
+}
+
 // qs slice of this lane: float4 chunks c8 + 8 i of sum_h q[b][g*G + h].
 template <typename T, int D>
 __device__ __forceinline__ void group_query(const SelectArgs &a, int b, int g, int c8, float4 (&qv)[D / 32]) {
