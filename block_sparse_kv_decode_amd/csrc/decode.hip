@@ -578,8 +578,9 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
 // Grid rows, bf16, for plans where one 256-thread workgroup scores and selects a row and a single
 // split attends it (many rows, short rows): the workgroup scores its row, selects (writing
 // agn_state and the selection), and attends the selected blocks straight after, so each row's
-// attention starts when its own selection is done rather than when the slowest row's is.  The
-// loads of the first two Gamma_e blocks go out before the Gamma_q ranking and land during it.
+// attention starts when its own selection is done rather than when the slowest row's is.  Rows
+// of up to 64 blocks are selected in registers (select_row64); on longer rows the loads of the
+// first two Gamma_e blocks go out before the Gamma_q ranking and land during it.
 template <int D, int G, int SPB>
 __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectArgs s) {
     extern __shared__ __align__(16) unsigned char dyn[];

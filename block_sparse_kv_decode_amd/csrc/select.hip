@@ -20,11 +20,12 @@
 //            and the blocks that left the window since (strict eviction);
 //   Gamma_q: top-kq by block score among the visible blocks outside Gamma_e.
 //   Exact top-k on unique 64-bit keys (order-preserving score bits, then the inverted block id,
-//   so equal scores go to the lower id): rows of up to 512 blocks rank every candidate against
-//   all others, several lanes sharing each count; longer rows first drop every key below a bound
-//   taken from the maxima of at most 256 chunks and rank the survivors (radix select as the
-//   fallback).  Outputs are compacted in ascending block id.  The selection's workgroup barriers
-//   wait for LDS only.
+//   so equal scores go to the lower id): rows of up to 64 blocks are ranked in registers, one
+//   block per lane, with the counting shared by the waves; rows of up to 512 blocks rank every
+//   candidate against all others in LDS, several lanes sharing each count; longer rows first drop
+//   every key below a bound taken from the maxima of at most 256 chunks and rank the survivors
+//   (radix select as the fallback).  Outputs are compacted in ascending block id.  The
+//   selection's workgroup barriers wait for LDS only.
 // Launch plans (chosen on the host).  "fused": one workgroup (256 or 1024 threads) scores a
 //   whole row and selects from LDS.  "parts": several workgroups (256 threads, or 1024 for rows
 //   over 1024 blocks) score slices of a row into the workspace while one more workgroup per row
