@@ -8,7 +8,7 @@ import torch
 pytestmark = pytest.mark.gpu
 
 import block_sparse_kv_decode_amd as N  # noqa: E402
-from nosa_inputs import generate, small_workload  # noqa: E402
+from nosa_inputs import f32_to_bf16_bits, generate, small_workload  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import gpuhelp as H  # noqa: E402
 
@@ -92,6 +92,48 @@ def test_select_ties_lowest_ids():
     sel, agn = H.gpu_select(shape, H.dev(x["q"]), kp, ev, N.workspace(shape))
     assert H.host(agn).tolist() == [[0, 1, 2, 3, 4]] * w.rows
     assert H.host(sel).tolist() == [list(range(11))] * w.rows
+
+
+@pytest.mark.parametrize("many", [False, True])
+def test_select_short_rows_match_general_topk_on_ties(many):
+    # Rows of up to 64 blocks are selected with one block per lane when one workgroup scores and
+    # selects a row (and in the one-launch step); scoring the same rows in two parts sends them
+    # through the general top-k instead.  Eviction scores on a coarse grid and pooled sub-block keys
+    # drawn from six vectors make many keys exactly equal, so the paths must agree on every tie
+    # (lower id first) with each other and with the oracle, on a fresh step and on a step with
+    # arrivals under strict eviction.
+    B, Hkv, G, d = (64, 4, 4, 64) if many else (2, 2, 4, 128)
+    n, extra, kq, ke = 48, 5, 6, 8
+    nbmax, R, k = n + extra, B * Hkv, kq + ke
+    rng = np.random.default_rng(4242 + int(many))
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hkv * G, d)).astype(np.float32))
+    vecs = rng.standard_normal((6, d)).astype(np.float32)
+    kp = np.ascontiguousarray(vecs[rng.integers(0, 6, size=(R, nbmax * 2))])
+    ev = (rng.integers(0, 5, size=(B, Hkv, nbmax)) / 4.0).astype(np.float32)
+    shape = N.make_shape(batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=d, n_blocks=n, n_blocks_max=nbmax,
+                         kq=kq, ke=ke, dtype=N.NOSA_BF16)
+    q_dev, kp_dev, ev_dev = H.dev(q), H.dev(kp), H.dev(ev)
+    ws, ws2 = N.workspace(shape), N.workspace(shape.copy(select_parts=2))
+    kp_ref = kp.reshape(B, Hkv, nbmax * 2, d).astype(np.float64)
+    kv = torch.zeros((B, Hkv, nbmax, 64, d), dtype=torch.bfloat16, device="cuda") if many else None
+    prev = prev2 = agn_ref = None
+    for n_prev, nn in ((0, n), (n, nbmax)):
+        sh = shape.copy(n_blocks=nn)
+        sel_a, agn_a = H.gpu_select(sh, q_dev, kp_dev, ev_dev, ws, n_prev=n_prev, agn=None if prev is None else prev.clone())
+        sel_b, agn_b = H.gpu_select(sh.copy(select_parts=2), q_dev, kp_dev, ev_dev, ws2, n_prev=n_prev,
+                                    agn=None if prev2 is None else prev2.clone())
+        assert torch.equal(sel_a, sel_b) and torch.equal(agn_a, agn_b), "step with n_prev %d" % n_prev
+        sel_r, agn_r, _ = O.select(O.block_scores(q, kp_ref, nn, 2), ev, kq, ke, n_prev, agn_ref)
+        assert np.array_equal(H.host(sel_a).reshape(B, Hkv, k), sel_r)
+        assert np.array_equal(H.host(agn_a).reshape(B, Hkv, ke), agn_r)
+        if many:   # 256 rows and one split per row: the one-launch step
+            agn_c = torch.full((R, ke), -7, dtype=torch.int32, device="cuda") if prev is None else prev.clone()
+            sel_c = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+            out = torch.empty((B, Hkv * G, d), dtype=torch.bfloat16, device="cuda")
+            N.nosa_decode_step(sh, q_dev, kp_dev, ev_dev, n_prev, agn_c, sel_c, kv, kv, nbmax, 0.125, out, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(sel_c, sel_a) and torch.equal(agn_c, agn_a)
+        prev, prev2, agn_ref = agn_a, agn_b, agn_r
 
 
 def test_select_planted_blocks():
