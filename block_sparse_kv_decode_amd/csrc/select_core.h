@@ -467,29 +467,47 @@ __device__ void select_row64(const SelectArgs &a, int row, const RowLds &L, int3
     for (int p = ns + i; p < k; p += 64) sel[p] = -1;
 }
 
-// qs slice of this lane: float4 chunks c8 + 8 i of sum_h q[b][g*G + h].
+// qs slice of this lane: float4 chunks c8 + 8 i of sum_h q[b][g*G + h].  For bf16 the heads are
+// read four at a time, the loads of a batch all issued before any is summed (heads past G re-read
+// the last head and are weighted 0), so G <= 4 costs one memory round trip rather than one per head.
 template <typename T, int D>
 __device__ __forceinline__ void group_query(const SelectArgs &a, int b, int g, int c8, float4 (&qv)[D / 32]) {
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) qv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sizeof(T) == 2) {
+        constexpr int kBatch = 4;
+        for (int h0 = 0; h0 < a.G; h0 += kBatch) {
+            uint2 u[kBatch][D / 32];
+#pragma unroll
+            for (int hh = 0; hh < kBatch; ++hh) {
+                const size_t base = (size_t)(b * a.Hq + g * a.G + min(h0 + hh, a.G - 1)) * D;
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i)
+                    u[hh][i] = *(const uint2 *)((const uint16_t *)a.q + base + (c8 + 8 * i) * 4);
+            }
+#pragma unroll
+            for (int hh = 0; hh < kBatch; ++hh) {
+                const float wt = h0 + hh < a.G ? 1.0f : 0.0f;   // no branch between loads and sums
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) {
+                    qv[i].x = fmaf(wt, bf16_lo(u[hh][i].x), qv[i].x);
+                    qv[i].y = fmaf(wt, bf16_hi(u[hh][i].x), qv[i].y);
+                    qv[i].z = fmaf(wt, bf16_lo(u[hh][i].y), qv[i].z);
+                    qv[i].w = fmaf(wt, bf16_hi(u[hh][i].y), qv[i].w);
+                }
+            }
+        }
+        return;
+    }
     for (int h = 0; h < a.G; ++h) {
         const size_t base = (size_t)(b * a.Hq + g * a.G + h) * D;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
-            const size_t e0 = base + (size_t)(c8 + 8 * i) * 4;
-            if (sizeof(T) == 2) {
-                const uint2 u = *(const uint2 *)((const uint16_t *)a.q + e0);
-                qv[i].x += bf16_lo(u.x);
-                qv[i].y += bf16_hi(u.x);
-                qv[i].z += bf16_lo(u.y);
-                qv[i].w += bf16_hi(u.y);
-            } else {
-                const float4 f = *(const float4 *)((const float *)a.q + e0);
-                qv[i].x += f.x;
-                qv[i].y += f.y;
-                qv[i].z += f.z;
-                qv[i].w += f.w;
-            }
+            const float4 f = *(const float4 *)((const float *)a.q + base + (size_t)(c8 + 8 * i) * 4);
+            qv[i].x += f.x;
+            qv[i].y += f.y;
+            qv[i].z += f.z;
+            qv[i].w += f.w;
         }
     }
 }
@@ -507,7 +525,10 @@ __device__ __forceinline__ void score_range(const SelectArgs &a, int row, int bl
     const int ngroups = (sb_hi - sb_lo + 7) >> 3;   // groups of 8 sub-blocks
     const float *kprow = a.kp + (size_t)row * a.n_blocks_max * SPB * D;
     float4 qv[CPLS];
-    group_query<T, D>(a, b, g, c8, qv);
+    // With 256 threads the group query is read after the first pass's pooled keys are requested, so
+    // its round trip overlaps theirs; 1024-thread workgroups (128 VGPRs) cannot hold both in flight.
+    bool have_q = NT > 256;
+    if (have_q) group_query<T, D>(a, b, g, c8, qv);
     for (int g0 = w; g0 < ngroups; g0 += NW * kUnroll) {
         float4 x[kUnroll][CPLS];
 #pragma unroll
@@ -517,6 +538,10 @@ __device__ __forceinline__ void score_range(const SelectArgs &a, int row, int bl
 #pragma unroll
             for (int i = 0; i < CPLS; ++i)
                 x[u][i] = v ? *(const float4 *)(kprow + (size_t)j * D + (c8 + 8 * i) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (!have_q) {
+            group_query<T, D>(a, b, g, c8, qv);
+            have_q = true;
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
