@@ -230,6 +230,28 @@ struct BlockAddr {
     }
 };
 
+// The MFMA B operand of a row's query: lane (j16, grp) holds dims 32 ks + 8 grp .. + 8 of head
+// j16 (zero for j16 >= G).  A caller that attends only after other work (scoring, ranking) loads
+// it first, so that the split's first K/V loads do not wait behind a query round trip.
+template <int D>
+struct QFrag {
+    bf16x8_t qb[D / 32];
+};
+
+template <int D, int G>
+__device__ __forceinline__ void load_qfrag(const DecodeArgs &a, int row, QFrag<D> &f) {
+    constexpr int RB = D * 2;
+    const int lane = threadIdx.x & 63, j16 = lane & 15, grp = lane >> 4;
+    const int b = row / a.Hkv, g = row - b * a.Hkv;
+    const char *qrow = (const char *)a.q + (size_t)(b * a.Hq + g * G + (j16 < G ? j16 : 0)) * RB;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (j16 < G) x = *(const uint4 *)(qrow + (4 * ks + grp) * 16);
+        f.qb[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+}
+
 // Two blocks whose loads a caller issued ahead of the split (the split's first two entries).
 template <int D>
 struct PreBlocks {
@@ -239,32 +261,30 @@ struct PreBlocks {
 
 // One split: entries [j0, j1) of the row's table (tab[j * tab_stride], block ids into the store),
 // written as partial slot sp of the row (or the output itself when a.direct).  With PRE, the loads
-// of entries j0 and j0 + 1 were already issued into *pre.
+// of entries j0 and j0 + 1 were already issued into *pre.  qf: the row's query fragment, loaded by
+// the caller (else loaded here).
 template <int D, int G, bool PRE = false>
 __device__ __forceinline__ void decode_mfma_split(const DecodeArgs &a, int row, int sp, const int32_t *tab,
                                                   int tab_stride, int j0, int j1, SplitShared<D, G> &sh,
-                                                  PreBlocks<D> *pre = nullptr) {
+                                                  PreBlocks<D> *pre = nullptr, const QFrag<D> *qf = nullptr) {
     using Gm = Geom<uint16_t, D>;
     constexpr int KS = D / 32;                        // 32-dim MFMA steps
-    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC, RB = Gm::RB;
+    constexpr int CPL = Gm::CPL, EPC = Gm::EPC, NC = Gm::NC;
     static_assert(CPL == KS, "bf16 rows: one V chunk per MFMA step");
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int j16 = lane & 15, grp = lane >> 4;       // MFMA layout: column (head) / k-group
     const int tpv = lane / NC;                        // PV layout
 
     // B operand: q of head j16 (zero columns beyond G), dims 32 ks + 8 grp .. + 8
-    bf16x8_t qb[KS];
-    {
-        const char *qrow = (const char *)a.q + (size_t)(b * a.Hq + g * G + (j16 < G ? j16 : 0)) * RB;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (j16 < G) x = *(const uint4 *)(qrow + (4 * ks + grp) * 16);
-            qb[ks] = __builtin_bit_cast(bf16x8_t, x);
-        }
+    QFrag<D> qown;
+    if (!qf) {
+        load_qfrag<D, G>(a, row, qown);
+        qf = &qown;
     }
+    bf16x8_t qb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = qf->qb[ks];
 
     const BlockAddr<D> ba(a, row);
 
@@ -535,6 +555,9 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
         return;
     }
     const int n = s.n_blocks, tid = threadIdx.x;
+    // the query fragment first: the split's first K/V loads then wait for nothing older
+    QFrag<D> qf;
+    load_qfrag<D, G>(a, row, qf);
     const RowLds L = carve<256>(dyn, n);
     int32_t *qlist = (int32_t *)(dyn + row_lds_bytes<256>(n));   // [kq] Gamma_q, ascending
     const float *gscore = s.scores + (size_t)row * s.scores_stride;
@@ -571,7 +594,7 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     const int j0 = (sp - S_e) * a.nbs, j1 = min(s.kq, j0 + a.nbs);
-    decode_mfma_split<D, G>(a, row, sp, qlist, 1, j0, j1, sh);
+    decode_mfma_split<D, G>(a, row, sp, qlist, 1, j0, j1, sh, nullptr, &qf);
 }
 
 // ---- the decode step in one workgroup per row ----------------------------------------------
@@ -590,6 +613,9 @@ __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectAr
     const int n = s.n_blocks, k = s.kq + s.ke;
     const RowLds L = carve<256>(dyn, n);
     int32_t *wl = (int32_t *)(dyn + row_lds_bytes<256>(n));   // [k]: Gamma_e, then Gamma_q, each ascending
+    // the query fragment first: attention's first K/V loads then wait for nothing older
+    QFrag<D> qf;
+    load_qfrag<D, G>(a, row, qf);
     float e[kEvPre];
     ev_load<256>(s, row, e);
     score_range<uint16_t, D, SPB, 256>(s, row, 0, n, L.sc, nullptr);
@@ -599,7 +625,7 @@ __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectAr
         // a row of up to 64 blocks: lane i of each wave holds block i, the waves share the ranking
         select_row64<256>(s, row, L, wl);
         wg_barrier();
-        decode_mfma_split<D, G>(a, row, 0, wl, 1, 0, k, sh);
+        decode_mfma_split<D, G>(a, row, 0, wl, 1, 0, k, sh, nullptr, &qf);
         return;
     }
     select_agnostic<256>(s, row, L, ssh);
@@ -619,9 +645,9 @@ __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectAr
     compact_outputs<256>(n, L.inQ, L.inQ, wl + s.ke, s.kq, nullptr, 0, ssh);
     wg_barrier();
     if (kPre && s.ke >= 2)
-        decode_mfma_split<D, G, kPre>(a, row, 0, wl, 1, 0, k, sh, &pre);
+        decode_mfma_split<D, G, kPre>(a, row, 0, wl, 1, 0, k, sh, &pre, &qf);
     else
-        decode_mfma_split<D, G>(a, row, 0, wl, 1, 0, k, sh);
+        decode_mfma_split<D, G>(a, row, 0, wl, 1, 0, k, sh, nullptr, &qf);
 }
 
 bool row_step_fits(int n_blocks, int k) {
