@@ -15,6 +15,7 @@ constexpr int kUnroll = 4;           // groups of eight sub-blocks per wave kept
 constexpr int kRankMaxBlocks = 512;  // rows up to this length use the one-pass rank selection
 constexpr int kCandMax = 512;        // candidates kept after the chunk-maximum bound
 constexpr int kEvPre = 4;            // eviction scores prefetched per thread
+constexpr int kScorePer = 4;         // block scores per thread loaded together by a Gamma_q ranking
 constexpr int kEvLdsMax = 4096;      // rows up to this length keep their eviction scores in LDS
 constexpr int kKeyScratch = 256 + kCandMax;   // uint64 LDS entries of the top-k scratch
 
