@@ -633,17 +633,18 @@ __global__ __launch_bounds__(256, 2) void row_step_kernel(DecodeArgs a, SelectAr
     load_qfrag<D, G>(a, row, qf);
     float e[kEvPre];
     ev_load<256>(s, row, e);
+    const int pid = prev_agn(s, row, n <= kWaveRowMax ? (int)(threadIdx.x & 63) : (int)threadIdx.x);
     score_range<uint16_t, D, SPB, 256>(s, row, 0, n, L.sc, nullptr);
     ev_store<256>(s, row, L, n, e);
     wg_barrier();
     if (n <= kWaveRowMax) {
         // a row of up to 64 blocks: lane i of each wave holds block i, the waves share the ranking
-        select_row64<256>(s, row, L, wl);
+        select_row64<256>(s, row, L, wl, pid);
         wg_barrier();
         decode_mfma_split<D, G>(a, row, 0, wl, 1, 0, k, sh, nullptr, &qf);
         return;
     }
-    select_agnostic<256>(s, row, L, ssh);
+    select_agnostic<256>(s, row, L, ssh, pid);
     compact_outputs<256>(n, L.inE, L.inE, wl, s.ke, nullptr, 0, ssh);
     wg_barrier();
     // The first two Gamma_e blocks' loads go out now and stay in flight through the Gamma_q

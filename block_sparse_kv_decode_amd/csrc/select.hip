@@ -44,16 +44,18 @@ __global__ __launch_bounds__(NT) void score_select_kernel(SelectArgs a) {
     __shared__ SelectShared<NT> sh;
     const int row = blockIdx.x;
     const RowLds L = carve<NT>(dyn, a.n_blocks);
+    const bool short_row = a.n_blocks <= kWaveRowMax;
     float e[kEvPre];
     ev_load<NT>(a, row, e);
+    const int pid = prev_agn(a, row, short_row ? (int)(threadIdx.x & 63) : (int)threadIdx.x);
     score_range<T, D, SPB, NT>(a, row, 0, a.n_blocks, L.sc, nullptr);
     ev_store<NT>(a, row, L, a.n_blocks, e);
     __syncthreads();
-    if (a.n_blocks <= kWaveRowMax) {   // a short row: one block per lane, ranked in registers
-        select_row64<NT>(a, row, L, nullptr);
+    if (short_row) {   // one block per lane, ranked in registers
+        select_row64<NT>(a, row, L, nullptr, pid);
         return;
     }
-    select_agnostic<NT>(a, row, L, sh);
+    select_agnostic<NT>(a, row, L, sh, pid);
     select_query<NT>(a, row, L, sh, true);
 }
 
@@ -75,10 +77,11 @@ __global__ __launch_bounds__(NT) void score_part_kernel(SelectArgs a) {
         const RowLds L = carve<NT>(dyn, a.n_blocks);
         float e[kEvPre];
         ev_load<NT>(a, row, e);
+        const int pid = prev_agn(a, row, threadIdx.x);
         ev_store<NT>(a, row, L, a.n_blocks, e);
         // The ranking shares its CU with the scoring workgroups: give it issue priority.
         __builtin_amdgcn_s_setprio(2);
-        select_agnostic<NT>(a, row, L, sh);
+        select_agnostic<NT>(a, row, L, sh, pid);
         compact_outputs<NT>(a.n_blocks, L.inE, L.inE, a.ke > 0 ? a.agn + (size_t)row * a.ke : nullptr, a.ke,
                             nullptr, 0, sh);
         return;

@@ -330,11 +330,19 @@ __device__ __forceinline__ void ev_store(const SelectArgs &a, int row, const Row
     for (int i = threadIdx.x + kEvPre * NT; i < n; i += NT) L.ev[i] = evr[i];
 }
 
+// Entry idx of the row's agn_state (the previous Gamma_e), or -1 on a fresh step or past ke.  The
+// selection kernels load it together with the eviction scores, so the previous members cost no
+// round trip of their own later.
+__device__ __forceinline__ int prev_agn(const SelectArgs &a, int row, int idx) {
+    return (a.n_prev > 0 && idx < a.ke) ? a.agn[(size_t)row * a.ke + idx] : -1;
+}
+
 // Gamma_e of one row into L.inE (all threads of the workgroup): the sink and window blocks plus
-// the score-ranked members under strict eviction.  Reads the previous Gamma_e from agn_state; uses
-// L.inQ as scratch and leaves it cleared.
+// the score-ranked members under strict eviction.  id0 = prev_agn(a, row, threadIdx.x); entries
+// past the first NT of the previous Gamma_e are read here.  Uses L.inQ as scratch and leaves it
+// cleared.
 template <int NT>
-__device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh) {
+__device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, SelectShared<NT> &sh, int id0) {
     const int tid = threadIdx.x;
     const int n = a.n_blocks;
     for (int i = tid; i < n; i += NT) {
@@ -346,11 +354,13 @@ __device__ void select_agnostic(const SelectArgs &a, int row, const RowLds &L, S
     const bool fresh = (n_prev == 0);
     const int w_lo = n - a.n_window;              // first window block
     const int left = n_prev - a.n_window;         // blocks below this were ranked (or out) last step
-    if (!fresh)
-        for (int j = tid; j < a.ke; j += NT) {
+    if (!fresh) {   // previous Gamma_e (inQ reused as scratch)
+        if (id0 >= 0 && id0 < n_prev) L.inQ[id0] = 1;
+        for (int j = tid + NT; j < a.ke; j += NT) {
             const int id = a.agn[(size_t)row * a.ke + j];
-            if (id >= 0 && id < n_prev) L.inQ[id] = 1;   // previous Gamma_e (inQ reused as scratch)
+            if (id >= 0 && id < n_prev) L.inQ[id] = 1;
         }
+    }
     for (int i = tid; i < n; i += NT)
         if (i < a.n_sink || i >= w_lo) L.inE[i] = 1;
     wg_barrier();
@@ -418,8 +428,9 @@ __device__ __forceinline__ int group_rank64(uint64_t key, int *part) {
 // the selection like select_query and, when wl is given, Gamma_e then Gamma_q (each ascending,
 // padded with -1 to ke and kq entries) to wl[0..k).  Reads L.sc and L.ev and uses L.keys as
 // scratch; called by all NT threads after the barrier that follows the scoring.
+// prev_id = prev_agn(a, row, lane).
 template <int NT>
-__device__ void select_row64(const SelectArgs &a, int row, const RowLds &L, int32_t *wl) {
+__device__ void select_row64(const SelectArgs &a, int row, const RowLds &L, int32_t *wl, int prev_id) {
     const int i = threadIdx.x & 63;
     const int n = a.n_blocks, ke = a.ke, kq = a.kq, k = kq + ke;
     const bool in_row = i < n;
@@ -429,7 +440,7 @@ __device__ void select_row64(const SelectArgs &a, int row, const RowLds &L, int3
     const bool fresh = (n_prev == 0);
     uint64_t prev = 0ull;
     if (!fresh && ke > 0) {
-        const int id = i < ke ? a.agn[(size_t)row * ke + i] : -1;
+        const int id = prev_id;
         const uint64_t has = __ballot(id >= 0 && id < n_prev);
         for (uint64_t m = has; m; m &= m - 1) {
             const int j = __builtin_ctzll(m);
