@@ -569,26 +569,7 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
         const int j = tid + r * 256;
         ids[r] = j < s.ke ? s.agn[(size_t)row * s.ke + j] : -1;
     }
-    float sv[kScorePer];   // up to kScorePer scores per thread loaded together, then stored
-#pragma unroll
-    for (int r = 0; r < kScorePer; ++r) {
-        const int i = tid + r * 256;
-        sv[r] = i < n ? gscore[i] : 0.0f;
-    }
-#pragma unroll
-    for (int r = 0; r < kScorePer; ++r) {
-        const int i = tid + r * 256;
-        if (i < n) {
-            L.sc[i] = sv[r];
-            L.inE[i] = 0;
-            L.inQ[i] = 0;
-        }
-    }
-    for (int i = tid + kScorePer * 256; i < n; i += 256) {
-        L.sc[i] = gscore[i];
-        L.inE[i] = 0;
-        L.inQ[i] = 0;
-    }
+    scores_to_lds<256>(gscore, n, L);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kAgnPer; ++r)

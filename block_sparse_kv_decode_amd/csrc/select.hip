@@ -103,27 +103,7 @@ __global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
     // the first NT Gamma_e ids are loaded together with the scores (one memory round trip) and
     // marked after the clear; any further ids are read after the barrier
     const int id0 = tid < a.ke ? agn[tid] : -1;
-    // up to kScorePer scores per thread are loaded together, then stored (one round trip)
-    float sv[kScorePer];
-#pragma unroll
-    for (int r = 0; r < kScorePer; ++r) {
-        const int i = tid + r * NT;
-        sv[r] = i < a.n_blocks ? gscore[i] : 0.0f;
-    }
-#pragma unroll
-    for (int r = 0; r < kScorePer; ++r) {
-        const int i = tid + r * NT;
-        if (i < a.n_blocks) {
-            L.sc[i] = sv[r];
-            L.inE[i] = 0;
-            L.inQ[i] = 0;
-        }
-    }
-    for (int i = tid + kScorePer * NT; i < a.n_blocks; i += NT) {
-        L.sc[i] = gscore[i];
-        L.inE[i] = 0;
-        L.inQ[i] = 0;
-    }
+    scores_to_lds<NT>(gscore, a.n_blocks, L);
     __syncthreads();
     if (id0 >= 0 && id0 < a.n_blocks) L.inE[id0] = 1;
     for (int j = tid + NT; j < a.ke; j += NT) {

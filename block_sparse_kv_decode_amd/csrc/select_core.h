@@ -330,6 +330,33 @@ __device__ __forceinline__ void ev_store(const SelectArgs &a, int row, const Row
     for (int i = threadIdx.x + kEvPre * NT; i < n; i += NT) L.ev[i] = evr[i];
 }
 
+// Copies a row's n block scores from global memory to L.sc and clears L.inE and L.inQ: up to
+// kScorePer scores per thread are loaded together before any is stored (one round trip).
+template <int NT>
+__device__ __forceinline__ void scores_to_lds(const float *gscore, int n, const RowLds &L) {
+    const int tid = threadIdx.x;
+    float sv[kScorePer];
+#pragma unroll
+    for (int r = 0; r < kScorePer; ++r) {
+        const int i = tid + r * NT;
+        sv[r] = i < n ? gscore[i] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < kScorePer; ++r) {
+        const int i = tid + r * NT;
+        if (i < n) {
+            L.sc[i] = sv[r];
+            L.inE[i] = 0;
+            L.inQ[i] = 0;
+        }
+    }
+    for (int i = tid + kScorePer * NT; i < n; i += NT) {
+        L.sc[i] = gscore[i];
+        L.inE[i] = 0;
+        L.inQ[i] = 0;
+    }
+}
+
 // Entry idx of the row's agn_state (the previous Gamma_e), or -1 on a fresh step or past ke.  The
 // selection kernels load it together with the eviction scores, so the previous members cost no
 // round trip of their own later.
