@@ -10,10 +10,11 @@
 //        is never selected again by the query-agnostic part; locality >= ke / k).
 //
 // Scoring.  Every lane builds its slice of the group query qs = sum of the row's G query heads
-//   (fp32) straight from global memory, so the pooled-key loads are issued without waiting on a
-//   barrier.  Eight lanes share one fp32 sub-block row (16-byte loads, 128 contiguous bytes per
-//   lane group and load), reduce with three DPP adds and max-pool the block's sub-blocks with DPP
-//   and lane swaps; each wave keeps four groups of eight rows in flight.
+//   (fp32) straight from global memory, no barrier involved; with 256 threads the pooled-key
+//   loads go out first and the query's loads (four heads at a time, all in flight) overlap them.
+//   Eight lanes share one fp32 sub-block row (16-byte loads, 128 contiguous bytes per lane group
+//   and load), reduce with three DPP adds and max-pool the block's sub-blocks with DPP and lane
+//   swaps; each wave keeps four groups of eight rows in flight.
 // Selection (one workgroup per row, in LDS).
 //   Gamma_e: the sink and window blocks (if any), plus the best blocks by eviction score among
 //            all other visible blocks (first step) or among the previous score-ranked members
