@@ -4,7 +4,9 @@ A step is one decode step of one attention layer for every sequence of the batch
 nosa_decode_step, which is nosa_select (pooled-key block scoring + query-agnostic / query-aware
 selection) followed by nosa_sparse_decode (split-K GQA attention over the selected blocks) in one
 call.  Pooled keys are state built once before timing (they change only when a block fills up).
-tokens/s = batch / step time.
+tokens/s = batch / step time.  The timed steps are fresh ones (n_blocks_prev = 0: the query-agnostic
+part ranks every visible block); ms_per_step_steady_state times the same step with n_blocks_prev =
+n_blocks, where it ranks the previous step's members under strict eviction.
 
   python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config C2] [--also C3,F1]
                   [--no-cpu-baseline] [--no-offload] [--no-transfer]
@@ -184,6 +186,13 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
         N.nosa_decode_step(shape, p["q"], p["kp"], p["ev"], 0, p["agn"], p["sel"], p["k"], p["v"], w.nbmax, scale,
                            p["out"], wsp, sh)
 
+    def steady(i):
+        """The same step in steady state: n_blocks_prev = n_blocks, so the query-agnostic part ranks
+        the previous step's members (agn_state, left by the fresh steps) under strict eviction."""
+        p = P[i % layers]
+        N.nosa_decode_step(shape, p["q"], p["kp"], p["ev"], w.n_blocks, p["agn"], p["sel"], p["k"], p["v"], w.nbmax,
+                           scale, p["out"], wsp, sh)
+
     def two_calls(i, evs=None):
         """The same step as nosa_select + nosa_sparse_decode, with events between the two calls."""
         p = P[i % layers]
@@ -209,7 +218,8 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
     # timed region 1: the plain step loop (headline value)
     wall_s = wall(step)
     res = {"wall_s": wall_s, "ms_per_step": 1e3 * wall_s / steps, "tokens_per_s": w.batch * steps / wall_s,
-           "layers": layers, "ms_per_step_two_calls": 1e3 * wall(two_calls) / steps}
+           "layers": layers, "ms_per_step_two_calls": 1e3 * wall(two_calls) / steps,
+           "ms_per_step_steady": 1e3 * wall(steady) / steps}
     if want_events:
         # A bounded spin kernel holds the stream while the host enqueues the event-timed steps, so
         # the GPU never waits on the host inside an event pair (Python can take longer to enqueue a
@@ -624,6 +634,7 @@ def main():
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": by["step"],
         "ms_per_step_two_calls": main_res["ms_per_step_two_calls"],
+        "ms_per_step_steady_state": main_res["ms_per_step_steady"],
         "step_ms_median_events": main_res["step_ms_median"],
         "step_ms_p10_p90_events": [main_res["step_ms_p10"], main_res["step_ms_p90"]],
         "roofline": {
@@ -642,6 +653,7 @@ def main():
         also[cfg] = {
             "workload": describe(r["workload"]), "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
             "ms_per_step_two_calls": r["ms_per_step_two_calls"],
+            "ms_per_step_steady_state": r["ms_per_step_steady"],
             "step_hbm_gbps": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
             "step_hbm_frac": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "decode_gbps": b2["decode"] / (r["decode_ms_mean"] * 1e-3) / 1e9,
