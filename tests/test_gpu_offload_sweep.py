@@ -4,6 +4,8 @@ and arriving blocks, the GPU's slot maps, block table, miss list and cache bytes
 oracle's cache simulation exactly, and attention over the cache must match the oracle's attention
 over the selected blocks."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -15,12 +17,13 @@ from nosa_inputs import f32_to_bf16_bits, generate, small_workload  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import gpuhelp as H  # noqa: E402
 
-N_CASES = 16
+# NOSA_SWEEP_CASES / NOSA_SWEEP_SEED widen the sweep (default: 16 cases, seed 31415)
+N_CASES = int(os.environ.get("NOSA_SWEEP_CASES", "16"))
 STEPS = 5
 
 
 def _cases():
-    rng = np.random.default_rng(31415)
+    rng = np.random.default_rng(int(os.environ.get("NOSA_SWEEP_SEED", "31415")))
     out = []
     for i in range(N_CASES):
         G = int(rng.choice([1, 2, 4, 8]))

@@ -8,6 +8,8 @@ Shapes vary over GQA groups 1 to 8, d 64 and 128, ragged budgets, empty query-aw
 query-agnostic subsets, and sink / window blocks. Each case runs a second step in which three
 blocks arrive under strict eviction."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,11 +21,12 @@ from nosa_inputs import generate, small_workload  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 from tests import gpuhelp as H  # noqa: E402
 
-N_CASES = 48
+# NOSA_SWEEP_CASES / NOSA_SWEEP_SEED widen the sweep (default: 48 cases, seed 20261203)
+N_CASES = int(os.environ.get("NOSA_SWEEP_CASES", "48"))
 
 
 def _cases():
-    rng = np.random.default_rng(20261203)
+    rng = np.random.default_rng(int(os.environ.get("NOSA_SWEEP_SEED", "20261203")))
     out = []
     for i in range(N_CASES):
         G = int(rng.choice([1, 2, 4, 8]))
