@@ -35,6 +35,7 @@ def _inputs(seed):
 
 def test_stores_beyond_4gib_step_and_two_calls_match_oracle_on_sampled_rows():
     need = 2 * B * HKV * NB * 64 * D * 2 + (6 << 30)
+    torch.cuda.empty_cache()                        # release what earlier tests left reserved
     free, _ = torch.cuda.mem_get_info()
     if free < need:
         pytest.skip("needs %.1f GiB of free device memory, %.1f GiB free" % (need / 2**30, free / 2**30))
@@ -71,3 +72,75 @@ def test_stores_beyond_4gib_step_and_two_calls_match_oracle_on_sampled_rows():
         ref = O.attention(q_r, k_r, v_r, sel_h[r].reshape(1, 1, kk))
         for out in (out1, out2):
             H.check_attention(H.host(out[b:b + 1, h * G:(h + 1) * G]), ref, "bf16", "row %d" % r)
+
+
+def test_offload_from_host_pool_beyond_4gib_matches_oracle():
+    # The pinned host pool holds 8 GiB per store; a cold step (every entry missed) and a step after
+    # a query drift (hits and misses) run through nosa_offload_decode with the gather on a copy
+    # stream.  Maps, tables, miss lists and every byte of the GPU cache follow the oracle's cache
+    # simulation and gather on all 256 rows; selection and attention are checked on sampled rows.
+    import psutil
+    C = 64
+    store = B * HKV * NB * 64 * D * 2
+    torch.cuda.empty_cache()                        # release what earlier tests left reserved
+    free, _ = torch.cuda.mem_get_info()
+    if free < 2 * store + (6 << 30) or psutil.virtual_memory().available < 3 * store + (8 << 30):
+        pytest.skip("needs 22 GiB of free device memory and 32 GiB of free host memory")
+    q, k, v, ev = _inputs(20261205)
+    shape = N.make_shape(batch=B, n_q_heads=HQ, n_kv_heads=HKV, head_dim=D, n_blocks=NB, n_blocks_max=NB,
+                         kq=KQ, ke=KE, sub_block_size=32, cache_slots=C, dtype=N.NOSA_BF16)
+    kp = H.gpu_pool(shape, k)
+    hk = torch.empty(k.shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(v.shape, dtype=torch.bfloat16, pin_memory=True)
+    hk.copy_(k)
+    hv.copy_(v)
+    del k, v
+    torch.cuda.empty_cache()
+    hk_h, hv_h = H.host(hk), H.host(hv)              # views of the pinned pool, no copy
+    R, kk = B * HKV, KQ + KE
+    ck = torch.zeros((B, HKV, C, 64, D), dtype=torch.bfloat16, device="cuda")
+    cv = torch.zeros_like(ck)
+    sob = torch.full((R, NB), -1, dtype=torch.int32, device="cuda")
+    bos = torch.full((R, C), -1, dtype=torch.int32, device="cuda")
+    table = torch.full((R, kk), -9, dtype=torch.int32, device="cuda")
+    mcnt = torch.full((R,), -9, dtype=torch.int32, device="cuda")
+    mlist = torch.full((R, kk, 2), -9, dtype=torch.int32, device="cuda")
+    sob_o, bos_o = np.full((R, NB), -1, np.int32), np.full((R, C), -1, np.int32)
+    ck_o, cv_o = np.zeros((B, HKV, C, 64, D), np.uint16), np.zeros((B, HKV, C, 64, D), np.uint16)
+    ws = N.workspace(shape)
+    copy = torch.cuda.Stream()
+    g = torch.Generator(device="cuda").manual_seed(7)
+    scale = 1.0 / np.sqrt(D)
+    ev_h = H.host(ev)
+    for t in range(2):
+        if t == 1:
+            q = (q.float() + 0.3 * torch.randn(q.shape, generator=g, device="cuda")).to(torch.bfloat16)
+        sel, agn = H.gpu_select(shape, q, kp, ev, ws)
+        out = torch.full((B, HQ, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        N.nosa_offload_decode(shape, q, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out, ws,
+                              copy=copy)
+        torch.cuda.synchronize()
+        sel_h, agn_h, q_h = H.host(sel), H.host(agn), H.host(q)
+        tab_o, mc_o, ml_o = O.cache_step(sel_h, sob_o, bos_o)
+        assert np.array_equal(H.host(sob), sob_o) and np.array_equal(H.host(bos), bos_o)
+        assert np.array_equal(H.host(table), tab_o) and np.array_equal(H.host(mcnt), mc_o)
+        ml = H.host(mlist)
+        used = np.arange(kk)[None, :] < mc_o[:, None]
+        assert np.array_equal(ml[used], ml_o[used])
+        if t == 0:
+            assert np.all(mc_o == kk)
+        else:
+            assert 0 < mc_o.sum() < R * kk
+        O.gather(mc_o.reshape(B, HKV), ml_o.reshape(B, HKV, kk, 2), hk_h, ck_o)
+        O.gather(mc_o.reshape(B, HKV), ml_o.reshape(B, HKV, kk, 2), hv_h, cv_o)
+        assert np.array_equal(H.host(ck), ck_o) and np.array_equal(H.host(cv), cv_o)
+        for r in ROWS:
+            b, h = divmod(r, HKV)
+            k_r = hk_h[b, h].reshape(1, 1, NB, 64, D)
+            v_r = hv_h[b, h].reshape(1, 1, NB, 64, D)
+            q_r = q_h[b:b + 1, h * G:(h + 1) * G]
+            s_ref = O.block_scores(q_r, O.pool_keys(k_r, 32), NB, 2)
+            H.check_selection(sel_h[r].reshape(1, 1, kk), agn_h[r].reshape(1, 1, KE), s_ref,
+                              ev_h[r].reshape(1, 1, NB), KQ, KE)
+            ref = O.attention(q_r, k_r, v_r, sel_h[r].reshape(1, 1, kk))
+            H.check_attention(H.host(out[b:b + 1, h * G:(h + 1) * G]), ref, "bf16", "step %d row %d" % (t, r))
