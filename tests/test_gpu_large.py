@@ -1,10 +1,11 @@
-"""K/V stores beyond 4 GiB: bs32 at 128K context (256 rows of 2048 blocks, 8 GiB per bf16 store),
-the size class a 288 GB device holds.  Row r of a store starts at r x 32 MiB, so rows from 64 on
-sit past 2^31 bytes and rows from 128 on past 2^31 elements: any 32-bit offset in pooling,
-scoring, selection or attention would wrap there.  The inputs follow the resident workloads'
-recipe (K noise plus per-block mean offsets, V ~ N(0, 1), eviction scores ~ U(0, 1)) but are drawn
-on the device with torch's seeded generator, since the host-side draw of 2 x 4.3e9 values would
-take minutes; the oracle recomputes each sampled row from host copies of the same inputs."""
+"""K/V stores beyond 4 GiB, through attention, selection, the offload gather and the append:
+bs32 at 128K context (256 rows of 2048 blocks, 8 GiB per bf16 store), the size class a 288 GB
+device holds.  Row r of a store starts at r x 32 MiB, so rows from 64 on sit past 2^31 bytes and
+rows from 128 on past 2^31 elements: any 32-bit offset in pooling, scoring, selection, attention,
+gather or append would wrap there.  The inputs follow the resident workloads' recipe (K noise
+plus per-block mean offsets, V ~ N(0, 1), eviction scores ~ U(0, 1)) but are drawn on the device
+with torch's seeded generator, since the host-side draw of 2 x 4.3e9 values would take minutes;
+the oracle recomputes each sampled row from host copies of the same inputs."""
 
 import numpy as np
 import pytest
@@ -144,3 +145,50 @@ def test_offload_from_host_pool_beyond_4gib_matches_oracle():
                               ev_h[r].reshape(1, 1, NB), KQ, KE)
             ref = O.attention(q_r, k_r, v_r, sel_h[r].reshape(1, 1, kk))
             H.check_attention(H.host(out[b:b + 1, h * G:(h + 1) * G]), ref, "bf16", "step %d row %d" % (t, r))
+
+
+def test_append_into_stores_beyond_4gib():
+    # The last sub-block of every row is written token by token through nosa_append_kv (32 calls);
+    # odd sequences skip the final token, so their sub-block stays open.  On the sampled rows the
+    # stores hold the appended tokens, and the pooled key of a closed sub-block equals the oracle's
+    # mean over the updated store (an open one keeps its old value).
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    need = 2 * B * HKV * NB * 64 * D * 2 + (4 << 30)
+    if free < need:
+        pytest.skip("needs %.1f GiB of free device memory, %.1f GiB free" % (need / 2**30, free / 2**30))
+    _, k, v, _ = _inputs(20261206)
+    shape = N.make_shape(batch=B, n_q_heads=HQ, n_kv_heads=HKV, head_dim=D, n_blocks=NB, n_blocks_max=NB,
+                         kq=KQ, ke=KE, sub_block_size=32, dtype=N.NOSA_BF16)
+    kp = H.gpu_pool(shape, k)
+    R = B * HKV
+    kp_before = kp.clone()
+    k_tail, v_tail = k[:, :, NB - 1, 63].clone(), v[:, :, NB - 1, 63].clone()
+    g = torch.Generator(device="cuda").manual_seed(11)
+    kn = torch.randn((32, B, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((32, B, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    acc = torch.full((R, D), float("nan"), dtype=torch.float32, device="cuda")
+    for i in range(32):
+        pos = torch.full((B,), NB * 64 - 32 + i, dtype=torch.int32, device="cuda")
+        if i == 31:
+            pos[1::2] = -1
+        N.nosa_append_kv(shape, kn[i], vn[i], pos, k, v, acc, kp)
+    torch.cuda.synchronize()
+    kn_h, vn_h = H.host(kn), H.host(vn)
+    for r in ROWS:
+        b, h = divmod(r, HKV)
+        k_r, v_r = H.host(k[b, h]), H.host(v[b, h])
+        closed = b % 2 == 0
+        n_new = 32 if closed else 31
+        assert np.array_equal(k_r[NB - 1, 32:32 + n_new], kn_h[:n_new, b, h])
+        assert np.array_equal(v_r[NB - 1, 32:32 + n_new], vn_h[:n_new, b, h])
+        if not closed:
+            assert np.array_equal(k_r[NB - 1, 63], H.host(k_tail[b, h]))
+            assert np.array_equal(v_r[NB - 1, 63], H.host(v_tail[b, h]))
+        kp_r = H.host(kp[r])
+        assert np.array_equal(kp_r[:-1], H.host(kp_before[r])[:-1])          # earlier sub-blocks untouched
+        if closed:
+            ref = O.pool_keys(k_r.reshape(1, 1, NB, 64, D), 32)[0, 0, -1]
+            np.testing.assert_allclose(kp_r[-1], ref, rtol=1e-6, atol=1e-6)
+        else:
+            assert np.array_equal(kp_r[-1], H.host(kp_before[r])[-1])
