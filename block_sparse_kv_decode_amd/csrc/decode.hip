@@ -537,9 +537,10 @@ __global__ __launch_bounds__(256, (G >= 8 || D > 64) ? 1 : 2) void decode_valu_k
 
 // ---- the decode step with the query-aware pick inside the attention launch -------------------
 // Grid rows x (S_e + S_q), bf16.  Once the scoring kernel has written the block scores and
-// Gamma_e (agn_state), a row's S_e first splits attend the Gamma_e blocks straight away, while each
-// of its S_q last splits ranks the row's Gamma_q in LDS (the first of them also writes the row's
-// selection, the ascending union) and then attends its slice of Gamma_q.  Attention does not
+// Gamma_e (agn_state), a row's S_e Gamma_e splits (partial slots 0 .. S_e - 1) attend the Gamma_e
+// blocks straight away, while each of its S_q Gamma_q splits (slots S_e ..) ranks the row's Gamma_q
+// in LDS (the one in slot S_e also writes the row's selection, the ascending union) and then
+// attends its slice of Gamma_q.  Attention does not
 // depend on the order of the blocks, so the pick hides under the Gamma_e splits' streaming instead
 // of taking a kernel of its own.  Every split writes partial slot sp; combine_kernel merges them.
 // Workgroup ids are split-major, Gamma_q splits first: ids [0, S_q * rows) are the Gamma_q splits
