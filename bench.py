@@ -34,10 +34,13 @@ sys.path.insert(0, ROOT)
 
 LAYERS = 4   # independent buffer sets the resident step rotates over (see run_resident)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
-# HBM bytes per launch from rocprofv3 counter runs: the attention call at bs16 / 16K (two kernels)
-# and the one-workgroup-per-row step kernel at bs64 / 4K
-PROFILE_TRAFFIC = {"C2": os.path.join(ROOT, "profiles", "decode_kernel_c2_traffic.json"),
-                   "C3": os.path.join(ROOT, "profiles", "step_kernel_c3_traffic.json")}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_path(cfg, kernel):
+    """Counter record of HBM bytes per launch of one kernel on one workload (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs scaled by the plain-copy calibration; written by --record-traffic)."""
+    return os.path.join(PROFILES, "traffic_%s_%s.json" % (kernel, cfg))
 # the sources the attention and step kernels are compiled from
 KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_kv_decode_amd", "csrc", f)
                for f in ("decode.hip", "select_core.h", "nosa_device.h", "nosa_internal.h")]
@@ -88,7 +91,18 @@ def algorithmic_bytes(w):
     ids = R * k * 4                                       # selected ids
     decode = kv_sel + q + o + ids                         # decode kernel: K/V, q, out, table
     select = kp + q + ev + ids + R * w.ke * 4             # select kernel: pooled keys, q, e, out ids + state
-    return {"step": kv_sel + kp + ev + q + o + ids, "decode": decode, "select": select}
+    step = kv_sel + kp + ev + q + o + ids
+    # The dominant kernel of nosa_decode_step, per launch (32 KiB of K + V per selected block at bf16 /
+    # d 128, times the R * k selected blocks, plus what else that kernel must read or write):
+    #   row_step_kernel     the whole step in one launch: the step's bytes;
+    #   step_decode_kernel  attention with the query-aware pick inside: K/V, q, each row's block
+    #                       scores and query-agnostic ids it ranks from, the selection it writes (the
+    #                       output is written by the merge kernel after it);
+    #   decode_*_kernel     attention of the two-call plan: K/V, q, the block ids (output by the merge).
+    kernel = {"row_step_kernel": step,
+              "step_decode_kernel": kv_sel + q + R * w.n_blocks * 4 + R * w.ke * 4 + ids,
+              "decode_mfma_kernel": kv_sel + q + ids, "decode_valu_kernel": kv_sel + q + ids}
+    return {"step": step, "decode": decode, "select": select, "kernel": kernel}
 
 
 class HipTimingEvents:
@@ -205,9 +219,10 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
         if evs is not None:
             T.record(evs[2], sh)
 
-    def wall(fn):
-        for i in range(warmup):
-            fn(i)
+    def wall(fn, warm=True):
+        if warm:
+            for i in range(warmup):
+                fn(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
@@ -215,10 +230,14 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    # timed region 1: the plain step loop (headline value)
+    # timed region 1: the plain step loop (headline value): `warmup` untimed steps, then exactly
+    # `steps` timed steps between two synchronisations
     wall_s = wall(step)
+    # the same region repeated (reported beside the headline, which stays the first region)
+    repeats = [1e3 * wall(step, warm=False) / steps for _ in range(3)]
     res = {"wall_s": wall_s, "ms_per_step": 1e3 * wall_s / steps, "tokens_per_s": w.batch * steps / wall_s,
-           "layers": layers, "ms_per_step_two_calls": 1e3 * wall(two_calls) / steps,
+           "ms_per_step_repeats": repeats, "layers": layers,
+           "ms_per_step_two_calls": 1e3 * wall(two_calls) / steps,
            "ms_per_step_steady": 1e3 * wall(steady) / steps}
     if want_events:
         # A bounded spin kernel holds the stream while the host enqueues the event-timed steps, so
@@ -228,8 +247,7 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
             torch.cuda.synchronize()
             torch.cuda._sleep(int(2.4e9 * (steps * 80e-6 + 2e-3)))
 
-        # timed region 2: the two-call step with events around each call (the attention call is
-        # the step's dominant kernel: the roofline figure)
+        # timed region 2: the two-call step with events around each call
         evs = [[T.create() for _ in range(3)] for _ in range(steps)]
         hold()
         for i in range(steps):
@@ -246,15 +264,64 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
             T.record(evs1[i][1], sh)
         torch.cuda.synchronize()
         stp_ms = [T.elapsed_ms(e[0], e[1]) for e in evs1]
+        # timed region 4: the step's dominant kernel alone, bracketed by the library's profiling
+        # hook (events recorded on the launch stream right before and after that kernel)
+        evs2 = [[T.create() for _ in range(2)] for _ in range(steps)]
+        hold()
+        names = set()
+        for i in range(steps):
+            N.nosa_profile_next_kernel(evs2[i][0].value, evs2[i][1].value)
+            step(i)
+            names.add(N.nosa_profile_last_kernel())
+        torch.cuda.synchronize()
+        assert len(names) == 1, names
+        ker_ms = [T.elapsed_ms(e[0], e[1]) for e in evs2]
         T.close()
         res.update({
             "select_ms_mean": statistics.mean(sel_ms), "decode_ms_mean": statistics.mean(dec_ms),
             "step_ms_median": statistics.median(stp_ms),
             "step_ms_p10": float(np.percentile(stp_ms, 10)), "step_ms_p90": float(np.percentile(stp_ms, 90)),
+            "kernel": names.pop(), "kernel_ms_mean": statistics.mean(ker_ms),
+            "kernel_ms_median": statistics.median(ker_ms),
         })
+    # The step's outputs, checked against the oracle: every buffer set holds a copy of the same layer,
+    # so every set's last step must give one result, bit for bit; set 0's is compared with the oracle.
+    torch.cuda.synchronize()
+    for t in sets[1:min(steps, layers)]:
+        assert torch.equal(t["sel"], sets[0]["sel"]) and torch.equal(t["agn"], sets[0]["agn"])
+        assert torch.equal(t["out"].view(torch.int16) if t["out"].dtype == torch.bfloat16 else t["out"],
+                           sets[0]["out"].view(torch.int16) if t["out"].dtype == torch.bfloat16 else sets[0]["out"])
+    res["outputs"] = {name: sets[0][name].cpu() for name in ("sel", "agn", "out")}
     res["bytes"] = algorithmic_bytes(w)
     res["workload"] = w
     return res
+
+
+def check_step_outputs(cfg, res):
+    """Compares the timed step's selection and output with the oracle on the same inputs: the
+    selection exactly (outside the 1e-4 relative tie band at the query-aware cut), the output
+    elementwise (bf16: |err| / max(|ref|, 1e-3) <= 1e-2 and mean |err| <= 2e-3).  Raises on a
+    mismatch; returns the error figures."""
+    import numpy as np
+    import torch
+
+    from nosa_inputs import WORKLOADS
+    from oracle import oracle as O
+    from tests.gpuhelp import check_attention, check_selection
+
+    w = WORKLOADS[cfg]
+    x = inputs(cfg)
+    t0 = time.perf_counter()
+    o = res["outputs"]
+    sel = o["sel"].numpy()
+    agn = o["agn"].numpy()[:, :w.ke]
+    out = o["out"].view(torch.int16).numpy().view(np.uint16) if o["out"].dtype == torch.bfloat16 else o["out"].numpy()
+    s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], 32), w.n_blocks, 2)
+    ties = check_selection(sel, agn, s_ref, x["evict"], w.kq, w.ke, n_sink=w.n_sink, n_window=w.n_window)
+    ref = O.attention(x["q"], x["k"], x["v"], sel.reshape(w.batch, w.n_kv_heads, w.k))
+    stats = check_attention(out, ref, w.dtype, cfg + " timed step")
+    return dict(checked=True, oracle="fp32 CPU oracle (selection and attention on the same inputs)",
+                tie_band_rows=ties, seconds=round(time.perf_counter() - t0, 2), **stats)
 
 
 def run_offload(steps_cap=None):
@@ -291,6 +358,7 @@ def run_offload(steps_cap=None):
     prompt_v[:, :, n0:] = 0
     hk, hv = pin(prompt_k), pin(prompt_v)
     del prompt_k, prompt_v
+    hkd, hvd = N.host_map(hk), N.host_map(hv)     # the pool's device addresses, resolved once
     kdev = bf16(x["k"]).cuda()
     shape0 = N.make_shape(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                           n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, cache_slots=w.cache_slots)
@@ -345,15 +413,15 @@ def run_offload(steps_cap=None):
             if phases:
                 evs[t][0].record(stream)
             if t > 0:
-                N.nosa_append_kv(shape0, new_k[t - 1], new_v[t - 1], positions[t], hk, hv, acc, kp, stream)
+                N.nosa_append_kv(shape0, new_k[t - 1], new_v[t - 1], positions[t], hkd, hvd, acc, kp, stream)
             N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
             if phases:
                 evs[t][1].record(stream)
             if overlap:
-                N.nosa_offload_decode(shape, qs[t], sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out,
-                                      ws, stream, copy_stream)
+                N.nosa_offload_decode(shape, qs[t], sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, scale,
+                                      out, ws, stream, copy_stream)
             else:
-                N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, stream, stream)
+                N.nosa_cache_update(shape, sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, stream, stream)
                 if phases:
                     evs[t][2].record(stream)
                 N.nosa_sparse_decode(shape, qs[t], ck, cv, C, table, scale, out, ws, stream)
@@ -515,9 +583,9 @@ def measure_link_peak():
 
 
 def cpu_baseline(cfg, budget_s=10.0, single_s=4.0, max_s=30.0):
-    """The CPU oracle (fp64, OpenMP over rows) on the same workload: scores + selection + attention
-    per step, repeated until about budget_s of wall time on every allowed core, then for about
-    single_s on one thread."""
+    """The CPU oracle (fp32, sequential sums, OpenMP over rows) on the same workload: scores +
+    selection + attention per step, repeated until about budget_s of wall time on every allowed core,
+    then for about single_s on one thread."""
     from nosa_inputs import WORKLOADS
     from oracle import oracle as O
 
@@ -543,25 +611,74 @@ def cpu_baseline(cfg, budget_s=10.0, single_s=4.0, max_s=30.0):
     reps, el = run(threads, budget_s)
     cores = O.get_threads()
     reps1, el1 = run(1, single_s)
+    O.set_threads(threads)
     step_bytes = algorithmic_bytes(w)["step"]
     return {"value": w.batch * reps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "%d full %s decode steps (block scores + selection + attention, all %d rows), "
-                      "%.1f s wall, fp64" % (reps, cfg, w.rows, el),
+                      "%.1f s wall, fp32 oracle" % (reps, cfg, w.rows, el),
             "effective_gbps": step_bytes * reps / el / 1e9,
             "single_thread": {"value": w.batch * reps1 / el1, "unit": "tokens/s",
                               "sample": "%d steps, %.1f s wall" % (reps1, el1)}}
 
 
-def traffic_record(cfg):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on this
-    workload and on the current kernel sources."""
-    path = PROFILE_TRAFFIC.get(cfg)
-    if path is None or not os.path.exists(path):
+def traffic_record(cfg, kernel):
+    """HBM bytes per launch of `kernel` on workload `cfg` from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources."""
+    path = traffic_path(cfg, kernel)
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_src_sha256") != kernel_src_sha256() or rec.get("workload") != cfg:
+    if rec.get("kernel_src_sha256") != kernel_src_sha256() or rec.get("workload") != cfg or \
+            rec.get("kernel") != kernel:
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_kib(csv_dir, counter, kernel):
+    """Mean value of `counter` per dispatch of the kernels whose name starts with `kernel`, from the
+    counter_collection CSV files rocprofv3 wrote under csv_dir."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            name = row.get("Kernel_Name", "")
+            base = name.split("(")[0].split("<")[0].split(" ")[-1].split("::")[-1]
+            if row.get("Counter_Name") == counter and base == kernel:
+                key = (f, row.get("Dispatch_Id"))
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s samples of %s under %s" % (counter, kernel, csv_dir))
+    return statistics.mean(vals.values()), len(vals)
+
+
+def record_traffic(cfg, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, commands):
+    """Writes profiles/traffic_<kernel>_<cfg>.json: FETCH_SIZE and WRITE_SIZE per dispatch of `kernel`
+    (KiB, from two rocprofv3 --pmc runs of the benchmark), each scaled by what the same counter reads
+    for a plain copy of 256 MiB read + 256 MiB written (bench.py --copy-calibration)."""
+    from nosa_inputs import WORKLOADS
+    fk, nf = _counter_kib(fetch_dir, "FETCH_SIZE", kernel)
+    wk, nw = _counter_kib(write_dir, "WRITE_SIZE", kernel)
+    cf, _ = _counter_kib(cal_fetch_dir, "FETCH_SIZE", "elementwise_kernel")
+    cw, _ = _counter_kib(cal_write_dir, "WRITE_SIZE", "elementwise_kernel")
+    true_kib = (64 << 20) * 4 / 1024.0
+    ff, wf = true_kib / cf, true_kib / cw
+    fetch_b, write_b = fk * 1024 * ff, wk * 1024 * wf
+    rec = {"workload": cfg, "kernel": kernel,
+           "what": "HBM bytes per dispatch of %s in nosa_decode_step on %s (%d / %d dispatches)" % (kernel, cfg, nf, nw),
+           "commands": commands,
+           "raw_kib_per_dispatch": {"FETCH_SIZE": fk, "WRITE_SIZE": wk},
+           "calibration": {"copy_kernel": "elementwise x*1 over 256 MiB float32 (reads and writes 268435456 B)",
+                           "FETCH_SIZE_kib": cf, "WRITE_SIZE_kib": cw, "fetch_factor": ff, "write_factor": wf},
+           "bytes_per_launch": int(round(fetch_b + write_b)), "fetch_bytes_per_launch": int(round(fetch_b)),
+           "write_bytes_per_launch": int(round(write_b)),
+           "algorithmic_bytes_per_launch": algorithmic_bytes(WORKLOADS[cfg])["kernel"][kernel],
+           "kernel_src_sha256": kernel_src_sha256(),
+           "kernel_src_hash_of": "decode.hip, select_core.h, nosa_device.h, nosa_internal.h with comments and "
+                                 "blank space removed"}
+    with open(traffic_path(cfg, kernel), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def describe(w):
@@ -570,6 +687,17 @@ def describe(w):
         extra = " (agnostic part incl. %d sink + %d window blocks)" % (w.n_sink, w.n_window)
     return "%s: B%d, GQA %d/%d, d%d, ctx %d, budget %d+%d blocks of 64 tokens%s, %s" % (
         w.name, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.kq, w.ke, extra, w.dtype)
+
+
+def kernel_roofline(cfg, r):
+    """Roofline entry of the step's dominant kernel: algorithmic bytes per launch over its mean
+    duration (HIP events from the library's profiling hook, on the launch stream)."""
+    kb = r["bytes"]["kernel"][r["kernel"]]
+    achieved = kb / (r["kernel_ms_mean"] * 1e-3) / 1e9
+    return {"kernel": r["kernel"], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(cfg, r["kernel"]),
+            "algorithmic_bytes_per_launch": kb, "avg_launch_ms": r["kernel_ms_mean"],
+            "median_launch_ms": r["kernel_ms_median"]}
 
 
 def main():
@@ -581,12 +709,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--also", default="C3,F1", help="comma list of extra resident workloads ('' for none)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-offload", action="store_true", help="skip the 128-step offload loop (C4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU timing and the check of the timed outputs)")
+    ap.add_argument("--no-offload", action="store_true", help="skip the 128-step offload loops (C4)")
     ap.add_argument("--no-transfer", action="store_true", help="skip the block- vs element-wise transfer sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise copy of 256 MiB (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=6, metavar=("CONFIG", "KERNEL", "FETCH_DIR", "WRITE_DIR",
+                                                          "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write profiles/traffic_<KERNEL>_<CONFIG>.json from rocprofv3 counter CSVs (no GPU)")
+    ap.add_argument("--record-commands", default="", help="';;'-separated commands quoted in the record")
     args = ap.parse_args()
+    if args.record_traffic:
+        cfg, kernel, fd, wd, cfd, cwd = args.record_traffic
+        record_traffic(cfg, kernel, fd, wd, cfd, cwd, [c for c in args.record_commands.split(";;") if c])
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (rows would shard "
               "across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
@@ -610,7 +747,6 @@ def main():
     w = main_res["workload"]
     by = main_res["bytes"]
     dec_s = main_res["decode_ms_mean"] * 1e-3
-    achieved = by["decode"] / dec_s / 1e9
     step_gbps = by["step"] / (main_res["ms_per_step"] * 1e-3) / 1e9
     line = {
         "metric": "sparse-decode tokens/s and achieved HBM GB/s (bs64 ctx4K, bs16 ctx16K)",
@@ -633,35 +769,36 @@ def main():
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": by["step"],
+        "ms_per_step_repeats": main_res["ms_per_step_repeats"],
         "ms_per_step_two_calls": main_res["ms_per_step_two_calls"],
         "ms_per_step_steady_state": main_res["ms_per_step_steady"],
         "step_ms_median_events": main_res["step_ms_median"],
         "step_ms_p10_p90_events": [main_res["step_ms_p10"], main_res["step_ms_p90"]],
-        "roofline": {
-            "kernel": "nosa_sparse_decode call: decode_mfma_kernel + combine_kernel (split-K merge)",
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(args.config),
-            "algorithmic_bytes_per_launch": by["decode"], "avg_launch_ms": main_res["decode_ms_mean"],
-        },
-        "select_kernel": {"avg_launch_ms": main_res["select_ms_mean"], "algorithmic_bytes": by["select"],
-                          "achieved_gbps": by["select"] / (main_res["select_ms_mean"] * 1e-3) / 1e9},
+        "roofline": kernel_roofline(args.config, main_res),
+        "two_call_attention": {
+            "kernels": "nosa_sparse_decode call: decode_mfma_kernel + combine_kernel (split-K merge)",
+            "avg_call_ms": main_res["decode_ms_mean"], "algorithmic_bytes": by["decode"],
+            "achieved_gbps": by["decode"] / dec_s / 1e9},
+        "select_call": {"avg_call_ms": main_res["select_ms_mean"], "algorithmic_bytes": by["select"],
+                        "achieved_gbps": by["select"] / (main_res["select_ms_mean"] * 1e-3) / 1e9},
     }
+    results = {args.config: main_res}
     also = {}
     for cfg in [c for c in args.also.split(",") if c]:
         r = run_resident(cfg, args.steps, args.warmup)
+        results[cfg] = r
         b2 = r["bytes"]
         also[cfg] = {
             "workload": describe(r["workload"]), "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+            "ms_per_step_repeats": r["ms_per_step_repeats"],
             "ms_per_step_two_calls": r["ms_per_step_two_calls"],
             "ms_per_step_steady_state": r["ms_per_step_steady"],
             "step_hbm_gbps": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
             "step_hbm_frac": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "decode_gbps": b2["decode"] / (r["decode_ms_mean"] * 1e-3) / 1e9,
-            "decode_avg_launch_ms": r["decode_ms_mean"], "select_avg_launch_ms": r["select_ms_mean"],
             "step_ms_median_events": r["step_ms_median"],
             "step_events_gbps": b2["step"] / (r["step_ms_median"] * 1e-3) / 1e9,
-            # counter-measured HBM bytes of the step kernel, where it is one launch (bs64 / 4K)
-            "step_traffic_bytes": traffic_record(cfg),
+            "roofline": kernel_roofline(cfg, r),
+            "two_call_decode_gbps": b2["decode"] / (r["decode_ms_mean"] * 1e-3) / 1e9,
         }
     if also:
         line["also"] = also
@@ -674,6 +811,13 @@ def main():
         line["transfer_granularity"] = run_transfer()
         line["transfer_granularity"]["link_peak_gbps_sdma"] = link if link is not None else measure_link_peak()
     if not args.no_cpu_baseline:
+        # the oracle leg: the timed outputs of every resident workload against the oracle (a mismatch
+        # ends the run without a result line), then the oracle's own timing on the headline workload
+        checks = {cfg: check_step_outputs(cfg, r) for cfg, r in results.items()}
+        line["checked"] = checks[args.config]
+        if also:
+            for cfg in also:
+                also[cfg]["checked"] = checks[cfg]
         line["cpu_baseline"] = cpu_baseline(args.config)
     print(json.dumps(line), flush=True)
 

@@ -4,6 +4,11 @@ Argument marshalling only: every function takes device tensors (anything with
 ``data_ptr()``), plain integers for pointers, or ``None`` for NULL, forwards them to the
 C entry point of the same name, and raises :class:`NosaError` on a non-zero status.  All
 work runs in the library's HIP kernels; there is no fallback path.
+
+Arguments that may live in pinned host memory (the offloaded KV pool) are passed to the library
+as device addresses.  A plain integer is taken to be one already (``host_map`` of the tensor,
+resolved once: the form for hot loops and graph capture); a CPU tensor is mapped on the spot with
+``nosa_host_map``.
 """
 
 from __future__ import annotations
@@ -28,7 +33,8 @@ NOSA_F32, NOSA_BF16 = 0, 1
 EXPORTED = (
     "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
     "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode", "nosa_offload_decode",
-    "nosa_gather_units", "nosa_decode_step",
+    "nosa_gather_units", "nosa_decode_step", "nosa_host_map", "nosa_profile_next_kernel",
+    "nosa_profile_last_kernel",
 )
 
 
@@ -99,6 +105,12 @@ def _load() -> ctypes.CDLL:
     L.nosa_offload_decode.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
     L.nosa_sparse_decode.restype = ctypes.c_int
     L.nosa_sparse_decode.argtypes = [SP, P, P, P, I32, P, ctypes.c_float, P, P, P]
+    L.nosa_host_map.restype = ctypes.c_int
+    L.nosa_host_map.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
+    L.nosa_profile_next_kernel.restype = ctypes.c_int
+    L.nosa_profile_next_kernel.argtypes = [P, P]
+    L.nosa_profile_last_kernel.restype = ctypes.c_char_p
+    L.nosa_profile_last_kernel.argtypes = []
     return L
 
 
@@ -112,6 +124,38 @@ def _p(x: Any) -> Optional[int]:
     if isinstance(x, int):
         return x
     return int(x.data_ptr())
+
+
+def nosa_host_map(x: Any) -> int:
+    """Device address of a buffer (device memory as is; pinned host memory: its device mapping)."""
+    out = ctypes.c_void_p()
+    _check(lib.nosa_host_map(_p(x), ctypes.byref(out)))
+    return int(out.value)
+
+
+def host_map(x: Any) -> int:
+    """Alias of nosa_host_map: resolve a host pool's device address once, outside hot loops."""
+    return nosa_host_map(x)
+
+
+def _dp(x: Any) -> Optional[int]:
+    """Device address of a buffer argument that may be pinned host memory: ints and None as given,
+    device tensors by data_ptr, CPU tensors through nosa_host_map."""
+    if x is None or isinstance(x, int):
+        return x
+    if getattr(x, "is_cuda", True):
+        return int(x.data_ptr())
+    return nosa_host_map(x)
+
+
+def nosa_profile_next_kernel(start: Any, stop: Any) -> None:
+    """Arm two HIP events (handles as ints, or None) for the next decode call on this thread."""
+    _check(lib.nosa_profile_next_kernel(start, stop))
+
+
+def nosa_profile_last_kernel() -> str:
+    """Kernel the last armed decode call timed (see nosa_profile_next_kernel)."""
+    return lib.nosa_profile_last_kernel().decode()
 
 
 def _stream(s: Any) -> Optional[int]:
@@ -150,7 +194,7 @@ def nosa_pool_keys(shape, k, first_block, n_new, pooled_k, stream=None) -> None:
 
 
 def nosa_append_kv(shape, k_new, v_new, positions, k_store, v_store, pool_acc, pooled_k, stream=None) -> None:
-    _check(lib.nosa_append_kv(ctypes.byref(shape), _p(k_new), _p(v_new), _p(positions), _p(k_store), _p(v_store),
+    _check(lib.nosa_append_kv(ctypes.byref(shape), _p(k_new), _p(v_new), _p(positions), _dp(k_store), _dp(v_store),
                               _p(pool_acc), _p(pooled_k), _stream(stream)))
 
 
@@ -168,7 +212,7 @@ def nosa_cache_update(shape, selected, slot_of_block, block_of_slot, block_table
     cs = _stream(compute)
     cp = cs if copy is None else _stream(copy)
     _check(lib.nosa_cache_update(ctypes.byref(shape), _p(selected), _p(slot_of_block), _p(block_of_slot),
-                                 _p(block_table), _p(miss_cnt), _p(miss_list), _p(host_k), _p(host_v),
+                                 _p(block_table), _p(miss_cnt), _p(miss_list), _dp(host_k), _dp(host_v),
                                  _p(cache_k), _p(cache_v), cs, cp))
 
 
@@ -190,13 +234,13 @@ def nosa_offload_decode(shape, q, selected, slot_of_block, block_of_slot, block_
     cs = _stream(compute)
     cp = cs if copy is None else _stream(copy)
     _check(lib.nosa_offload_decode(ctypes.byref(shape), _p(q), _p(selected), _p(slot_of_block), _p(block_of_slot),
-                                   _p(block_table), _p(miss_cnt), _p(miss_list), _p(host_k), _p(host_v),
+                                   _p(block_table), _p(miss_cnt), _p(miss_list), _dp(host_k), _dp(host_v),
                                    _p(cache_k), _p(cache_v), ctypes.c_float(softmax_scale), _p(out), _p(ws), cs, cp))
 
 
 def nosa_gather_units(src, src_units, dst, dst_units, unit_bytes, src_unit, dst_unit, n_units,
                       stream=None) -> None:
-    _check(lib.nosa_gather_units(_p(src), int(src_units), _p(dst), int(dst_units), int(unit_bytes), _p(src_unit),
+    _check(lib.nosa_gather_units(_dp(src), int(src_units), _dp(dst), int(dst_units), int(unit_bytes), _p(src_unit),
                                  _p(dst_unit), int(n_units), _stream(stream)))
 
 

@@ -215,31 +215,24 @@ int get_events(DeviceEvents **out) {
     return NOSA_OK;
 }
 
-// Device address of a caller buffer: device memory as is, pinned host memory through its device
-// mapping.  Pageable host memory is rejected.
-int device_address(const void *p, void **out, const char *what) {
-    hipPointerAttribute_t attr;
-    hipError_t e = hipPointerGetAttributes(&attr, p);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(NOSA_EINVAL, "%s is neither device memory nor pinned host memory (%s)", what, hipGetErrorString(e));
+// One-shot pair of timing events per host thread: armed by nosa_profile_next_kernel, recorded
+// around the dominant kernel of the next decode call on this thread, then disarmed.
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+thread_local const char *g_prof_kernel = "";
+
+struct ProfileMarks {
+    hipEvent_t start = nullptr, stop = nullptr;
+    ProfileMarks() {
+        start = g_prof_start;
+        stop = g_prof_stop;
+        g_prof_start = g_prof_stop = nullptr;
+        if (start) g_prof_kernel = "";
     }
-    if (attr.type == hipMemoryTypeHost) {
-        void *d = nullptr;
-        e = hipHostGetDevicePointer(&d, const_cast<void *>(p), 0);
-        if (e != hipSuccess || !d) {
-            (void)hipGetLastError();
-            return fail(NOSA_EINVAL, "%s: pinned host memory without a device mapping (%s)", what, hipGetErrorString(e));
-        }
-        *out = d;
-        return NOSA_OK;
+    // names the kernel the marks bracket (when armed)
+    void timed(const char *kernel) const {
+        if (start) g_prof_kernel = kernel;
     }
-    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged || attr.type == hipMemoryTypeUnified) {
-        *out = const_cast<void *>(p);
-        return NOSA_OK;
-    }
-    return fail(NOSA_EINVAL, "%s is neither device memory nor pinned host memory", what);
-}
+};
 
 }  // namespace
 
@@ -247,7 +240,43 @@ extern "C" {
 
 const char *nosa_last_error(void) { return g_err; }
 
-const char *nosa_version(void) { return "nosa-mi355x 0.1 (gfx950)"; }
+const char *nosa_version(void) { return "nosa-mi355x 0.2 (gfx950)"; }
+
+int nosa_host_map(const void *ptr, void **device_address) {
+    if (!device_address) return fail(NOSA_EINVAL, "device_address is NULL");
+    *device_address = nullptr;
+    if (!ptr) return fail(NOSA_EINVAL, "ptr is NULL");
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NOSA_EINVAL, "ptr is neither device memory nor pinned host memory (%s)", hipGetErrorString(e));
+    }
+    if (attr.type == hipMemoryTypeHost) {
+        void *d = nullptr;
+        e = hipHostGetDevicePointer(&d, const_cast<void *>(ptr), 0);
+        if (e != hipSuccess || !d) {
+            (void)hipGetLastError();
+            return fail(NOSA_EINVAL, "pinned host memory without a device mapping (%s)", hipGetErrorString(e));
+        }
+        *device_address = d;
+        return ok();
+    }
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged || attr.type == hipMemoryTypeUnified) {
+        *device_address = const_cast<void *>(ptr);
+        return ok();
+    }
+    return fail(NOSA_EINVAL, "ptr is neither device memory nor pinned host memory");
+}
+
+const char *nosa_profile_last_kernel(void) { return g_prof_kernel; }
+
+int nosa_profile_next_kernel(hipEvent_t start, hipEvent_t stop) {
+    if ((start == nullptr) != (stop == nullptr)) return fail(NOSA_EINVAL, "start and stop must both be set or both NULL");
+    g_prof_start = start;
+    g_prof_stop = stop;
+    return ok();
+}
 
 size_t nosa_workspace_bytes(const nosa_shape *shape) {
     if (check_shape(shape) != NOSA_OK) return 0;
@@ -288,15 +317,12 @@ int nosa_append_kv(const nosa_shape *shape, const void *k_new, const void *v_new
     REQUIRE_PTR(v_store, 16);
     REQUIRE_PTR(pool_acc, 16);
     REQUIRE_PTR(pooled_k, 16);
-    void *dk = nullptr, *dv = nullptr;
-    if ((rc = device_address(k_store, &dk, "k_store")) != NOSA_OK) return rc;
-    if ((rc = device_address(v_store, &dv, "v_store")) != NOSA_OK) return rc;
     AppendArgs a;
     a.k_new = k_new;
     a.v_new = v_new;
     a.positions = positions;
-    a.k_store = dk;
-    a.v_store = dv;
+    a.k_store = k_store;
+    a.v_store = v_store;
     a.acc = pool_acc;
     a.kp = pooled_k;
     a.Hkv = shape->n_kv_heads;
@@ -318,13 +344,9 @@ int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst
     REQUIRE_PTR(dst, 16);
     REQUIRE_PTR(src_unit, 4);
     REQUIRE_PTR(dst_unit, 4);
-    void *ds = nullptr, *dd = nullptr;
-    int rc;
-    if ((rc = device_address(src, &ds, "src")) != NOSA_OK) return rc;
-    if ((rc = device_address(dst, &dd, "dst")) != NOSA_OK) return rc;
     UnitsArgs a;
-    a.src = (const unsigned char *)ds;
-    a.dst = (unsigned char *)dd;
+    a.src = (const unsigned char *)src;
+    a.dst = (unsigned char *)dst;
     a.src_unit = src_unit;
     a.dst_unit = dst_unit;
     a.n_units = n_units;
@@ -433,18 +455,6 @@ static int cache_step(const nosa_shape *shape, const int32_t *selected, int32_t 
     REQUIRE_PTR(cache_k, 16);
     REQUIRE_PTR(cache_v, 16);
 
-    void *dk = nullptr, *dv = nullptr;
-    hipError_t e = hipHostGetDevicePointer(&dk, const_cast<void *>(host_k), 0);
-    if (e != hipSuccess || !dk) {
-        (void)hipGetLastError();
-        return fail(NOSA_EINVAL, "host_k is not pinned, device-mapped host memory (%s)", hipGetErrorString(e));
-    }
-    e = hipHostGetDevicePointer(&dv, const_cast<void *>(host_v), 0);
-    if (e != hipSuccess || !dv) {
-        (void)hipGetLastError();
-        return fail(NOSA_EINVAL, "host_v is not pinned, device-mapped host memory (%s)", hipGetErrorString(e));
-    }
-
     const int R = rows_of(shape);
     CacheArgs c;
     c.sel = selected;
@@ -457,12 +467,12 @@ static int cache_step(const nosa_shape *shape, const int32_t *selected, int32_t 
     c.k = k;
     c.C = shape->cache_slots;
     c.nbmax = shape->n_blocks_max;
-    e = launch_cache_map(c, R, compute);
+    hipError_t e = launch_cache_map(c, R, compute);
     if (e != hipSuccess) return hip_fail(e, "cache_map launch");
 
     GatherArgs g;
-    g.hk = (const unsigned char *)dk;
-    g.hv = (const unsigned char *)dv;
+    g.hk = (const unsigned char *)host_k;
+    g.hv = (const unsigned char *)host_v;
     g.ck = (unsigned char *)cache_k;
     g.cv = (unsigned char *)cache_v;
     g.mcnt = miss_cnt;
@@ -579,9 +589,14 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
                      int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, const void *k_store,
                      const void *v_store, int32_t store_blocks, float softmax_scale, void *out, void *ws,
                      hipStream_t stream) {
+    const ProfileMarks pm;   // consumed by this call, whatever its outcome
     int rc = check_shape(shape);
     if (rc) return rc;
     if ((rc = check_decode_args(q, k_store, v_store, store_blocks, softmax_scale, out, ws)) != NOSA_OK) return rc;
+    if (store_blocks < shape->n_blocks)
+        return fail(NOSA_EINVAL, "store_blocks %d is below n_blocks %d: the selection would name blocks outside the "
+                    "store", store_blocks, shape->n_blocks);
+    const KernelMarks km{pm.start, pm.stop};
     const PartPlan pp = select_plan(shape);
     const SplitPlan dp = decode_plan(shape);
     // The pick moves into the attention launch when the selection would otherwise need its own
@@ -599,8 +614,9 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
             return rc;
         DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
         a.table = selected;
+        pm.timed("row_step_kernel");
         hipError_t e = launch_row_step(shape->head_dim, group_of(shape), spb_of(shape), a, sa, rows_of(shape),
-                                       stream);
+                                       stream, km);
         return e == hipSuccess ? ok() : hip_fail(e, "decode_step launch");
     }
     if (!fused) {
@@ -608,7 +624,9 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
             return rc;
         DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
         a.table = selected;
-        hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream, true);
+        pm.timed(shape->dtype == NOSA_BF16 ? "decode_mfma_kernel" : "decode_valu_kernel");
+        hipError_t e =
+            launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream, true, km);
         return e == hipSuccess ? ok() : hip_fail(e, "decode_step attention launch");
     }
     SelectArgs sa;
@@ -622,20 +640,24 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
     a.St = S_e + S_q;
     a.s0 = 0;
     a.direct = 0;
-    hipError_t e = launch_step_decode(shape->head_dim, group_of(shape), a, sa, rows_of(shape), S_e, S_q, stream);
+    pm.timed("step_decode_kernel");
+    hipError_t e = launch_step_decode(shape->head_dim, group_of(shape), a, sa, rows_of(shape), S_e, S_q, stream, km);
     return e == hipSuccess ? ok() : hip_fail(e, "decode_step launch");
 }
 
 int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_store, const void *v_store,
                        int32_t store_blocks, const int32_t *block_table, float softmax_scale, void *out, void *ws,
                        hipStream_t stream) {
+    const ProfileMarks pm;   // consumed by this call, whatever its outcome
     int rc = check_shape(shape);
     if (rc) return rc;
     REQUIRE_PTR(block_table, 4);
     if ((rc = check_decode_args(q, k_store, v_store, store_blocks, softmax_scale, out, ws)) != NOSA_OK) return rc;
     DecodeArgs a = decode_args(shape, q, k_store, v_store, store_blocks, softmax_scale, out, ws);
     a.table = block_table;
-    hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream, true);
+    pm.timed(shape->dtype == NOSA_BF16 ? "decode_mfma_kernel" : "decode_valu_kernel");
+    hipError_t e = launch_decode(shape->dtype, shape->head_dim, group_of(shape), a, rows_of(shape), stream, true,
+                                 KernelMarks{pm.start, pm.stop});
     return e == hipSuccess ? ok() : hip_fail(e, "sparse_decode launch");
 }
 

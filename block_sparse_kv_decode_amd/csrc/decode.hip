@@ -181,7 +181,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, int row, int s
             }
         }
         if (a.direct) {
-            store_elem<T>(a.out, out_base + idx, A / L);
+            store_elem<T>(a.out, out_base + idx, L > 0.0f ? A / L : 0.0f);   // a row with no valid block: 0
         } else {
             float *part = a.part + ((size_t)(row * a.St + a.s0 + sp) * G + h) * (D + 2);
             part[2 + dd] = A;
@@ -704,42 +704,52 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
         }
         M = mc;
     }
-    store_elem<T>(a.out, (size_t)(b * a.Hq + g * G + h) * D + dd, A / L);
+    // a row with no valid block in any slot (L = 0) yields 0
+    store_elem<T>(a.out, (size_t)(b * a.Hq + g * G + h) * D + dd, L > 0.0f ? A / L : 0.0f);
 }
 
+static hipError_t mark(hipEvent_t ev, hipStream_t st) { return ev ? hipEventRecord(ev, st) : hipSuccess; }
+
 template <typename T, int D, int G>
-static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st, bool merge) {
+static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st, bool merge, const KernelMarks &m) {
+    hipError_t e = mark(m.start, st);
+    if (e != hipSuccess) return e;
     if (sizeof(T) == 2)
         decode_mfma_kernel<D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
     else
         decode_valu_kernel<D, G><<<dim3((unsigned)(rows * a.S)), dim3(256), 0, st>>>(a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(m.stop, st);
     if (e != hipSuccess || a.direct || !merge) return e;
     combine_kernel<T, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_d(int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge) {
+static hipError_t launch_decode_d(int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge,
+                                  const KernelMarks &m) {
     switch (G) {
-        case 1: return launch_decode_t<T, D, 1>(a, rows, st, merge);
-        case 2: return launch_decode_t<T, D, 2>(a, rows, st, merge);
-        case 4: return launch_decode_t<T, D, 4>(a, rows, st, merge);
-        default: return launch_decode_t<T, D, 8>(a, rows, st, merge);
+        case 1: return launch_decode_t<T, D, 1>(a, rows, st, merge, m);
+        case 2: return launch_decode_t<T, D, 2>(a, rows, st, merge, m);
+        case 4: return launch_decode_t<T, D, 4>(a, rows, st, merge, m);
+        default: return launch_decode_t<T, D, 8>(a, rows, st, merge, m);
     }
 }
 
 template <int D, int G>
 static hipError_t launch_step_t(const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
-                                hipStream_t st) {
+                                hipStream_t st, const KernelMarks &m) {
     const size_t dyn = row_lds_bytes<256>(s.n_blocks) + 4 * (size_t)s.kq;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)step_decode_kernel<D, G>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
+    hipError_t e = mark(m.start, st);
+    if (e != hipSuccess) return e;
     step_decode_kernel<D, G><<<dim3((unsigned)(rows * (S_e + S_q))), dim3(256), dyn, st>>>(a, s, S_e, S_q);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(m.stop, st);
     if (e != hipSuccess) return e;
     combine_kernel<uint16_t, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
     return hipGetLastError();
@@ -747,64 +757,73 @@ static hipError_t launch_step_t(const DecodeArgs &a, const SelectArgs &s, int ro
 
 template <int D>
 static hipError_t launch_step_d(int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
-                                hipStream_t st) {
+                                hipStream_t st, const KernelMarks &m) {
     switch (G) {
-        case 1: return launch_step_t<D, 1>(a, s, rows, S_e, S_q, st);
-        case 2: return launch_step_t<D, 2>(a, s, rows, S_e, S_q, st);
-        case 4: return launch_step_t<D, 4>(a, s, rows, S_e, S_q, st);
-        default: return launch_step_t<D, 8>(a, s, rows, S_e, S_q, st);
+        case 1: return launch_step_t<D, 1>(a, s, rows, S_e, S_q, st, m);
+        case 2: return launch_step_t<D, 2>(a, s, rows, S_e, S_q, st, m);
+        case 4: return launch_step_t<D, 4>(a, s, rows, S_e, S_q, st, m);
+        default: return launch_step_t<D, 8>(a, s, rows, S_e, S_q, st, m);
     }
 }
 
 hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
-                              hipStream_t st) {
-    return d == 128 ? launch_step_d<128>(G, a, s, rows, S_e, S_q, st) : launch_step_d<64>(G, a, s, rows, S_e, S_q, st);
+                              hipStream_t st, const KernelMarks &m) {
+    return d == 128 ? launch_step_d<128>(G, a, s, rows, S_e, S_q, st, m)
+                    : launch_step_d<64>(G, a, s, rows, S_e, S_q, st, m);
 }
 
 template <int D, int G, int SPB>
-static hipError_t launch_row_step_t(const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st) {
+static hipError_t launch_row_step_t(const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st,
+                                    const KernelMarks &m) {
     const size_t dyn = row_lds_bytes<256>(s.n_blocks) + 4 * (size_t)(s.kq + s.ke);
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)row_step_kernel<D, G, SPB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
+    hipError_t e = mark(m.start, st);
+    if (e != hipSuccess) return e;
     row_step_kernel<D, G, SPB><<<dim3((unsigned)rows), dim3(256), dyn, st>>>(a, s);
-    return hipGetLastError();
+    e = hipGetLastError();
+    return e == hipSuccess ? mark(m.stop, st) : e;
 }
 
 template <int D, int G>
-static hipError_t launch_row_step_g(int spb, const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st) {
+static hipError_t launch_row_step_g(int spb, const DecodeArgs &a, const SelectArgs &s, int rows, hipStream_t st,
+                                    const KernelMarks &m) {
     switch (spb) {
-        case 1: return launch_row_step_t<D, G, 1>(a, s, rows, st);
-        case 2: return launch_row_step_t<D, G, 2>(a, s, rows, st);
-        case 4: return launch_row_step_t<D, G, 4>(a, s, rows, st);
-        default: return launch_row_step_t<D, G, 8>(a, s, rows, st);
+        case 1: return launch_row_step_t<D, G, 1>(a, s, rows, st, m);
+        case 2: return launch_row_step_t<D, G, 2>(a, s, rows, st, m);
+        case 4: return launch_row_step_t<D, G, 4>(a, s, rows, st, m);
+        default: return launch_row_step_t<D, G, 8>(a, s, rows, st, m);
     }
 }
 
 template <int D>
 static hipError_t launch_row_step_d(int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
-                                    hipStream_t st) {
+                                    hipStream_t st, const KernelMarks &m) {
     switch (G) {
-        case 1: return launch_row_step_g<D, 1>(spb, a, s, rows, st);
-        case 2: return launch_row_step_g<D, 2>(spb, a, s, rows, st);
-        case 4: return launch_row_step_g<D, 4>(spb, a, s, rows, st);
-        default: return launch_row_step_g<D, 8>(spb, a, s, rows, st);
+        case 1: return launch_row_step_g<D, 1>(spb, a, s, rows, st, m);
+        case 2: return launch_row_step_g<D, 2>(spb, a, s, rows, st, m);
+        case 4: return launch_row_step_g<D, 4>(spb, a, s, rows, st, m);
+        default: return launch_row_step_g<D, 8>(spb, a, s, rows, st, m);
     }
 }
 
 hipError_t launch_row_step(int d, int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
-                           hipStream_t st) {
-    return d == 128 ? launch_row_step_d<128>(G, spb, a, s, rows, st) : launch_row_step_d<64>(G, spb, a, s, rows, st);
+                           hipStream_t st, const KernelMarks &m) {
+    return d == 128 ? launch_row_step_d<128>(G, spb, a, s, rows, st, m)
+                    : launch_row_step_d<64>(G, spb, a, s, rows, st, m);
 }
 
 // merge: run combine_kernel over the St partial slots after this launch (unless direct).
-hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge) {
+hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge,
+                         const KernelMarks &m) {
     if (dtype == 1)
-        return d == 128 ? launch_decode_d<uint16_t, 128>(G, a, rows, st, merge)
-                        : launch_decode_d<uint16_t, 64>(G, a, rows, st, merge);
-    return d == 128 ? launch_decode_d<float, 128>(G, a, rows, st, merge) : launch_decode_d<float, 64>(G, a, rows, st, merge);
+        return d == 128 ? launch_decode_d<uint16_t, 128>(G, a, rows, st, merge, m)
+                        : launch_decode_d<uint16_t, 64>(G, a, rows, st, merge, m);
+    return d == 128 ? launch_decode_d<float, 128>(G, a, rows, st, merge, m)
+                    : launch_decode_d<float, 64>(G, a, rows, st, merge, m);
 }
 
 }  // namespace nosa

@@ -100,6 +100,12 @@ struct DecodeArgs {
     float sl2;            // softmax scale * log2(e)
 };
 
+// Optional timing events recorded on the launch stream immediately before and after the attention
+// kernel of a decode launcher (nullptr: none).  The profiling hook of the C ABI arms them.
+struct KernelMarks {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Each launcher returns hipSuccess or the error of the launch.
 hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_t st);
 hipError_t launch_append(int dtype, int d, const AppendArgs &a, int rows, hipStream_t st);
@@ -110,14 +116,15 @@ hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int row
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t st);
 hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st);
-hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge);
+hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge,
+                         const KernelMarks &marks = KernelMarks());
 // bf16 decode step after a no_pick selection launch: attention over Gamma_e (S_e splits per row) and
 // over Gamma_q ranked in the same launch (S_q splits), then the merge of the S_e + S_q partials.
 hipError_t launch_step_decode(int d, int G, const DecodeArgs &a, const SelectArgs &s, int rows, int S_e, int S_q,
-                              hipStream_t st);
+                              hipStream_t st, const KernelMarks &marks = KernelMarks());
 // bf16 decode step in one workgroup per row: scoring, selection and single-split attention.
 hipError_t launch_row_step(int d, int G, int spb, const DecodeArgs &a, const SelectArgs &s, int rows,
-                           hipStream_t st);
+                           hipStream_t st, const KernelMarks &marks = KernelMarks());
 // Dynamic LDS of the one-workgroup-per-row step (the row's selection state plus its k-entry work
 // list) within this bound, which leaves room for two workgroups per CU in the 160 KiB of LDS.
 constexpr size_t kRowStepMaxLds = 56 * 1024;

@@ -42,6 +42,9 @@ class OffloadStepGraphs:
         self.k_new = torch.zeros((B, Hkv, d), dtype=dt, device="cuda")
         self.v_new = torch.zeros((B, Hkv, d), dtype=dt, device="cuda")
         self.positions = torch.zeros((B,), dtype=torch.int32, device="cuda")
+        # the host pool's device addresses, resolved once: the captured calls make no pointer query
+        self.hk = N.host_map(state["host_k"])
+        self.hv = N.host_map(state["host_v"])
         self.graphs: Dict[Tuple[int, int, bool], torch.cuda.CUDAGraph] = {}
 
     def enqueue(self, n_blocks: int, n_prev: int, append: bool, stream=None) -> None:
@@ -49,11 +52,11 @@ class OffloadStepGraphs:
         s = self.s
         shape = self.shape0.copy(n_blocks=n_blocks)
         if append:
-            N.nosa_append_kv(self.shape0, self.k_new, self.v_new, self.positions, s["host_k"], s["host_v"],
-                             s["pool_acc"], s["pooled_k"], stream)
+            N.nosa_append_kv(self.shape0, self.k_new, self.v_new, self.positions, self.hk, self.hv, s["pool_acc"],
+                             s["pooled_k"], stream)
         N.nosa_select(shape, self.q, s["pooled_k"], s["evict"], n_prev, s["agn"], s["selected"], s["ws"], stream)
         N.nosa_offload_decode(shape, self.q, s["selected"], s["slot_of_block"], s["block_of_slot"], s["block_table"],
-                              s["miss_cnt"], s["miss_list"], s["host_k"], s["host_v"], s["cache_k"], s["cache_v"],
+                              s["miss_cnt"], s["miss_list"], self.hk, self.hv, s["cache_k"], s["cache_v"],
                               self.scale, s["out"], s["ws"], stream, self.copy)
 
     def replay(self, n_blocks: int, n_prev: int, append: bool) -> None:
@@ -61,9 +64,9 @@ class OffloadStepGraphs:
         g = self.graphs.get(key)
         if g is None:
             g = torch.cuda.CUDAGraph()
-            # relaxed: the entry points query pointer attributes and host-pool mappings on the host
-            # while they enqueue; nothing they call synchronises or allocates
-            with torch.cuda.graph(g, capture_error_mode="relaxed"):
+            # default (global) capture mode: the calls only enqueue kernels and event record / wait
+            # pairs; the host pool mapping was resolved before capture
+            with torch.cuda.graph(g):
                 self.enqueue(n_blocks, n_prev, append)
             self.graphs[key] = g
         g.replay()

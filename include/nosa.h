@@ -21,8 +21,10 @@
  *
  * Conventions for every entry point
  *   - All buffers are owned by the caller.  Device pointers point to GPU memory of the current
- *     HIP device; host pools are pinned (page-locked, device-mapped) host memory.  The library
- *     allocates no memory.
+ *     HIP device.  Host pools are pinned (page-locked) host memory, passed to the per-step calls as
+ *     the device address that nosa_host_map returned for them once: the per-step calls make no
+ *     pointer query of their own, so they can be captured into a HIP graph in strict mode.  The
+ *     library allocates no memory.
  *   - Calls only enqueue work on the given stream(s) and never synchronise the host.
  *   - Shapes, pointers and alignment are validated on the host before any HIP call; a rejected
  *     call returns a negative nosa_status, launches nothing and leaves every buffer untouched.
@@ -88,6 +90,32 @@ const char *nosa_last_error(void);
 /* Library build identifier (compile target and version string). */
 const char *nosa_version(void);
 
+/*
+ * Device address of a caller buffer, resolved once so that the per-step calls need no pointer
+ * query ([P1] §4: the transfer kernel reads host memory through unified virtual addressing).
+ *   ptr            : device memory (returned as is) or pinned host memory (its device mapping)
+ *   device_address : out; NULL on failure
+ * Errors: NOSA_EINVAL for NULL arguments, pageable host memory or an unknown pointer.  Call it
+ * outside graph capture (it queries the HIP runtime); the address stays valid while the buffer
+ * stays allocated.
+ */
+int nosa_host_map(const void *ptr, void **device_address);
+
+/*
+ * Profiling hook.  Arms two HIP events for the next nosa_decode_step or nosa_sparse_decode call on
+ * the calling host thread: that call records `start` on its stream immediately before launching its
+ * dominant kernel (the attention launch; the whole step when it is one launch) and `stop`
+ * immediately after it, before any merge kernel.  The call consumes the pair whatever its outcome;
+ * both NULL disarms.  With events created by the caller (e.g. with hipEventDisableSystemFence, so
+ * that they do not flush caches), hipEventElapsedTime then gives that kernel's duration on the
+ * stream it ran on.  Errors: NOSA_EINVAL if exactly one of the two is NULL.
+ */
+int nosa_profile_next_kernel(hipEvent_t start, hipEvent_t stop);
+
+/* Name of the kernel that the last call consuming an armed pair bracketed with it (e.g.
+ * "step_decode_kernel"), or "" if that call launched nothing.  Per host thread; never NULL. */
+const char *nosa_profile_last_kernel(void);
+
 /* Device workspace bytes needed by nosa_select / nosa_block_scores / nosa_sparse_decode /
  * nosa_offload_decode for this shape (the same workspace serves all four; it is larger when
  * cache_slots >= kq + ke, for the offload path).  Returns 0 if the shape is invalid (see
@@ -120,8 +148,8 @@ int nosa_pool_keys(const nosa_shape *shape, const void *k, int32_t first_block, 
  *   k_new, v_new : device, [B, Hkv, d], dtype
  *   positions    : device, [B] int32; rows whose position lies outside [0, n_blocks_max * block_size)
  *                  are skipped
- *   k_store, v_store : [B, Hkv, n_blocks_max, block_size, d], dtype; device memory, or pinned host
- *                  memory (written through its device mapping: the offloaded host pool)
+ *   k_store, v_store : [B, Hkv, n_blocks_max, block_size, d], dtype; device memory, or the device
+ *                  address (nosa_host_map) of pinned host memory: the offloaded host pool
  *   pool_acc     : device, [B, Hkv, d] float32, running sums of the open sub-blocks (state kept by
  *                  the caller between calls; no initial contents needed)
  *   pooled_k     : device, as in nosa_pool_keys
@@ -189,8 +217,8 @@ int nosa_select(const nosa_shape *shape, const void *q, const float *pooled_k, c
  *   block_table   : device, [B, Hkv, k] int32, out: the slot holding selected[i]
  *   miss_cnt      : device, [B, Hkv] int32, out
  *   miss_list     : device, [B, Hkv, k, 2] int32, out: (block, slot) of the first miss_cnt misses
- *   host_k/host_v : pinned host memory, [B, Hkv, n_blocks_max, block_size, d], dtype; the library
- *                   reads it through its device mapping (hipHostGetDevicePointer)
+ *   host_k/host_v : the device addresses (nosa_host_map) of the pinned host pool,
+ *                   [B, Hkv, n_blocks_max, block_size, d], dtype, read by the gather kernel
  *   cache_k/cache_v : device, [B, Hkv, C, block_size, d], dtype; missed blocks are copied in
  *   compute       : stream of the map update; copy : stream of the block transfer (may equal
  *                   compute or be NULL = compute).  On return, work later enqueued on `compute`
@@ -217,7 +245,8 @@ int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t 
  *              (store_blocks = n_blocks_max, table = selected) or the GPU cache
  *              (store_blocks = cache_slots, table = block_table of nosa_cache_update)
  *   block_table : device, [B, Hkv, k] int32 with k = kq + ke; entries outside [0, store_blocks)
- *              are skipped
+ *              are skipped; a row with no entry inside the store gets an output of 0 (attention
+ *              over an empty set of tokens is undefined; 0 is the value that carries nothing)
  *   out      : device, [B, Hq, d], dtype
  *   ws       : device workspace
  */
@@ -228,7 +257,9 @@ int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_sto
 /*
  * One whole decode step on GPU-resident KV: nosa_select followed by nosa_sparse_decode over the
  * selection ([P1] App. A: select, then attend; §2.1 and §3.1 for the selection).  Arguments as for
- * the two calls (table = selected).  agn_state, selected and out come out as from the two calls:
+ * the two calls (table = selected), except that store_blocks must be at least n_blocks (every
+ * selected id names a block of the store; NOSA_EINVAL otherwise).  agn_state, selected and out come
+ * out as from the two calls:
  * selected and agn_state exactly, out up to float32 summation order.  When the selection would
  * score a row in several workgroups and rank Gamma_q in a kernel of its own (rows of more than
  * 64 KiB of pooled keys and fewer than 256 rows; bf16; kq, ke > 0; n_blocks <= 512), the ranking
@@ -251,15 +282,14 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
  * [dst_unit[u] * unit_bytes, +unit_bytes) of dst.  With unit_bytes = one KV block per head
  * (16 KiB at 64 tokens x d 128 x bf16) this is the block gather of nosa_cache_update; with the
  * bytes of one token's key or value it is an element-wise gather.
- *   src, src_units : pinned host memory (read through its device mapping) or device memory,
+ *   src, src_units : device address (nosa_host_map) of pinned host memory, or device memory,
  *               holding src_units units
- *   dst, dst_units : device memory (or pinned host memory) holding dst_units units
+ *   dst, dst_units : device memory (or the device address of pinned host memory), dst_units units
  *   unit_bytes: power of two in [16, 1 MiB]
  *   src_unit, dst_unit : device, [n_units] int32 unit indices; a pair with either index outside
  *               its buffer is skipped; dst_unit entries must be distinct (else which copy lands is
  *               undefined)
- * n_units == 0 is a no-op.  Errors: NOSA_EINVAL for a bad size, a NULL or misaligned pointer, or
- * memory that is neither device memory nor pinned host memory.
+ * n_units == 0 is a no-op.  Errors: NOSA_EINVAL for a bad size or a NULL or misaligned pointer.
  */
 int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst_units, int64_t unit_bytes,
                       const int32_t *src_unit, const int32_t *dst_unit, int64_t n_units, hipStream_t stream);

@@ -12,11 +12,15 @@
  * The pages print no equations; every formula below is the plainest reading of
  * their prose, and each function names the passage it follows.
  *
- * Arithmetic: inputs (fp32, bf16 bit patterns, or fp64) are widened exactly to
- * double, and every sum runs sequentially in double, in index order.  No
- * blocking, fusion or reordering.  Rows (batch x KV head) are independent and
- * are spread over OpenMP threads; each row is computed serially, so results do
- * not depend on the thread count.
+ * Arithmetic: one accumulator type, acc_t, for every value the method computes.
+ * The default build is float32, the precision the oracle's contract names: inputs
+ * (fp32, or bf16 bit patterns widened exactly) are used as fp32, and every sum
+ * runs sequentially in fp32, in index order.  Compiled with -DORACLE_F64 the same
+ * source accumulates in double instead (fp64 inputs then pass through unrounded);
+ * the tests hold the two builds against each other to bound the fp32 build's
+ * rounding.  No blocking, fusion or reordering.  Rows (batch x KV head) are
+ * independent and are spread over OpenMP threads; each row is computed serially,
+ * so results do not depend on the thread count.
  *
  * Error convention: functions return 0 on success and a negative number on an
  * input they cannot process (the Python wrapper raises on it).
@@ -29,20 +33,36 @@
 #include <omp.h>
 #endif
 
+#ifdef ORACLE_F64
+typedef double acc_t;
+#define ACC_EXP exp
+#define ACC_BITS 64
+#else
+typedef float acc_t;
+#define ACC_EXP expf
+#define ACC_BITS 32
+#endif
+
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 
-/* Exact widening of one input element to double. */
-static double elem(const void *p, int dtype, size_t i)
+/* Bits of the accumulator type of this build (32 or 64). */
+int oracle_acc_bits(void)
+{
+    return ACC_BITS;
+}
+
+/* One input element as acc_t: bf16 and fp32 exactly; an fp64 input is rounded in the fp32 build. */
+static acc_t elem(const void *p, int dtype, size_t i)
 {
     if (dtype == OR_F32)
-        return (double)((const float *)p)[i];
+        return (acc_t)((const float *)p)[i];
     if (dtype == OR_BF16) {
         uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
         float f;
         memcpy(&f, &u, sizeof f);
-        return (double)f;
+        return (acc_t)f;
     }
-    return ((const double *)p)[i];
+    return (acc_t)((const double *)p)[i];
 }
 
 void oracle_set_threads(int n)
@@ -69,11 +89,11 @@ int oracle_get_threads(void)
  * the first of the two pooling stages averages the keys of each sub-block.
  *
  *   K  : [rows][n_tokens][d]            (n_tokens = whole blocks)
- *   Kp : [rows][n_tokens / sbs][d]      double
+ *   Kp : [rows][n_tokens / sbs][d]      acc_t
  *   Kp[r][j][c] = (1/sbs) * sum_{t = j*sbs}^{j*sbs+sbs-1} K[r][t][c]
  */
 int oracle_pool_keys(int64_t rows, int64_t n_tokens, int d, int sbs,
-                     const void *K, int kdtype, double *Kp)
+                     const void *K, int kdtype, acc_t *Kp)
 {
     if (rows < 0 || n_tokens < 0 || d <= 0 || sbs <= 0 || n_tokens % sbs != 0)
         return -1;
@@ -82,10 +102,10 @@ int oracle_pool_keys(int64_t rows, int64_t n_tokens, int d, int sbs,
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t j = 0; j < nsub; j++) {
             for (int c = 0; c < d; c++) {
-                double sum = 0.0;
+                acc_t sum = 0;
                 for (int t = 0; t < sbs; t++)
                     sum += elem(K, kdtype, ((size_t)r * n_tokens + (size_t)(j * sbs + t)) * d + c);
-                Kp[((size_t)r * nsub + j) * d + c] = sum / (double)sbs;
+                Kp[((size_t)r * nsub + j) * d + c] = sum / (acc_t)sbs;
             }
         }
     }
@@ -101,14 +121,14 @@ int oracle_pool_keys(int64_t rows, int64_t n_tokens, int d, int sbs,
  * the sum of its heads' dot products; the block score is the maximum over the
  * block's sub-blocks.  No scale and no softmax (a positive scale keeps the ranks).
  *
- *   q  : [B][Hq][d]       Kp : [B*Hkv][kp_stride][d] (double, from oracle_pool_keys)
- *   s  : [B*Hkv][n_blocks] double
+ *   q  : [B][Hq][d]       Kp : [B*Hkv][kp_stride][d] (acc_t, from oracle_pool_keys)
+ *   s  : [B*Hkv][n_blocks] acc_t
  *   u[j]  = sum_{h = g*G}^{g*G+G-1} ( sum_c q[b][h][c] * Kp[b,g][j][c] )
  *   s[i]  = max_{j = i*spb}^{i*spb+spb-1} u[j]
  */
 int oracle_block_scores(int B, int Hq, int Hkv, int d, int n_blocks, int spb,
-                        const void *q, int qdtype, const double *Kp, int64_t kp_stride,
-                        double *s)
+                        const void *q, int qdtype, const acc_t *Kp, int64_t kp_stride,
+                        acc_t *s)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || n_blocks < 0 || spb <= 0 ||
         kp_stride < (int64_t)n_blocks * spb)
@@ -119,12 +139,12 @@ int oracle_block_scores(int B, int Hq, int Hkv, int d, int n_blocks, int spb,
     for (int64_t r = 0; r < R; r++) {
         const int b = (int)(r / Hkv), g = (int)(r % Hkv);
         for (int i = 0; i < n_blocks; i++) {
-            double best = 0.0;
+            acc_t best = 0;
             for (int jj = 0; jj < spb; jj++) {
                 const int64_t j = (int64_t)i * spb + jj;
-                double u = 0.0;
+                acc_t u = 0;
                 for (int h = g * G; h < g * G + G; h++) {
-                    double dot = 0.0;
+                    acc_t dot = 0;
                     for (int c = 0; c < d; c++)
                         dot += elem(q, qdtype, ((size_t)b * Hq + h) * d + c) *
                                Kp[((size_t)r * kp_stride + j) * d + c];
@@ -145,7 +165,7 @@ int oracle_block_scores(int B, int Hq, int Hkv, int d, int n_blocks, int spb,
  * ascending order with a strict comparison keeps the lower id on equal keys.
  * Returns 0, or -1 if fewer than kk candidates exist.
  */
-static int topk_plain(int n, const double *key, const uint8_t *cand, int kk, uint8_t *chosen)
+static int topk_plain(int n, const acc_t *key, const uint8_t *cand, int kk, uint8_t *chosen)
 {
     for (int round = 0; round < kk; round++) {
         int best = -1;
@@ -183,7 +203,7 @@ static int topk_plain(int n, const double *key, const uint8_t *cand, int kk, uin
  * formed first, then Gamma_q from its complement).
  * Ties on e or s go to the lower block id.
  *
- *   s         : [R][n_blocks] double        e : [R][e_stride] float32 (first n_blocks used)
+ *   s         : [R][n_blocks] acc_t         e : [R][e_stride] float32 (first n_blocks used)
  *   agn_state : [R][ke] int32  in: Gamma_e(t-1) (ignored when n_prev == 0); out: Gamma_e(t), ascending
  *   selected  : [R][kq+ke] int32 out: Gamma_e(t) U Gamma_q(t), ascending
  *   is_agn    : [R][kq+ke] uint8 out (may be NULL): 1 where selected[i] came from Gamma_e
@@ -191,7 +211,7 @@ static int topk_plain(int n, const double *key, const uint8_t *cand, int kk, uin
  * n_prev >= n_sink + n_window.
  */
 int oracle_select_sw(int64_t R, int n_blocks, int kq, int ke, int n_sink, int n_window, int n_prev,
-                     const double *s, const float *e, int64_t e_stride,
+                     const acc_t *s, const float *e, int64_t e_stride,
                      int32_t *agn_state, int32_t *selected, uint8_t *is_agn)
 {
     const int k = kq + ke;
@@ -209,11 +229,11 @@ int oracle_select_sw(int64_t R, int n_blocks, int kq, int ke, int n_sink, int n_
         uint8_t *inE = calloc((size_t)n_blocks, 1);
         uint8_t *candQ = calloc((size_t)n_blocks, 1);
         uint8_t *inQ = calloc((size_t)n_blocks, 1);
-        double *ekey = malloc(sizeof(double) * (size_t)n_blocks);
+        acc_t *ekey = malloc(sizeof(acc_t) * (size_t)n_blocks);
         int bad = (!prevE || !candE || !inE || !candQ || !inQ || !ekey);
         if (!bad) {
             for (int i = 0; i < n_blocks; i++)
-                ekey[i] = (double)e[(size_t)r * e_stride + i];
+                ekey[i] = (acc_t)e[(size_t)r * e_stride + i];   /* exact: fp32 values */
             if (n_prev > 0) {
                 for (int j = 0; j < ke; j++) {
                     int id = agn_state[(size_t)r * ke + j];
@@ -271,7 +291,7 @@ int oracle_select_sw(int64_t R, int n_blocks, int kq, int ke, int n_sink, int n_
 
 /* The selection without sink and window blocks: every query-agnostic member is score-ranked. */
 int oracle_select(int64_t R, int n_blocks, int kq, int ke, int n_prev,
-                  const double *s, const float *e, int64_t e_stride,
+                  const acc_t *s, const float *e, int64_t e_stride,
                   int32_t *agn_state, int32_t *selected, uint8_t *is_agn)
 {
     return oracle_select_sw(R, n_blocks, kq, ke, 0, 0, n_prev, s, e, e_stride, agn_state, selected, is_agn);
@@ -391,24 +411,25 @@ int oracle_gather(int64_t R, int k, int C, int nbmax, int64_t block_bytes,
  *
  *   q     : [B][Hq][d]                      query head h reads KV head g = h / (Hq/Hkv)
  *   Ks,Vs : [B*Hkv][store_blocks][bs][d]    table : [B*Hkv][k] indices into the store
- *   out   : [B][Hq][d] double
+ *   out   : [B][Hq][d] acc_t
  *   z_t = scale * q.K_t ;  w_t = exp(z_t - max z) ;  out = sum_t w_t V_t / sum_t w_t
  */
 int oracle_attention(int B, int Hq, int Hkv, int d, int bs, int k, int store_blocks,
                      const void *q, int qdtype, const void *Ks, const void *Vs, int kvdtype,
-                     const int32_t *table, double scale, double *out)
+                     const int32_t *table, double scale, acc_t *out)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || bs <= 0 || k <= 0 ||
         store_blocks <= 0)
         return -1;
     const int G = Hq / Hkv;
     const int T = k * bs;
+    const acc_t sc = (acc_t)scale;
     int status = 0;
 #pragma omp parallel for schedule(dynamic) reduction(min : status)
     for (int64_t bh = 0; bh < (int64_t)B * Hq; bh++) {
         const int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
         const int64_t r = (int64_t)b * Hkv + g;
-        double *z = malloc(sizeof(double) * (size_t)T);
+        acc_t *z = malloc(sizeof(acc_t) * (size_t)T);
         if (!z) {
             status = -2;
             continue;
@@ -422,24 +443,24 @@ int oracle_attention(int B, int Hq, int Hkv, int d, int bs, int k, int store_blo
             }
             for (int t = 0; t < bs; t++) {
                 const size_t kv = (((size_t)r * store_blocks + blk) * bs + t) * d;
-                double dot = 0.0;
+                acc_t dot = 0;
                 for (int c = 0; c < d; c++)
                     dot += elem(q, qdtype, (size_t)bh * d + c) * elem(Ks, kvdtype, kv + c);
-                z[i * bs + t] = scale * dot;
+                z[i * bs + t] = sc * dot;
             }
         }
         if (!bad) {
-            double m = z[0];
+            acc_t m = z[0];
             for (int t = 1; t < T; t++)
                 if (z[t] > m)
                     m = z[t];
-            double l = 0.0;
+            acc_t l = 0;
             for (int t = 0; t < T; t++) {
-                z[t] = exp(z[t] - m);
+                z[t] = ACC_EXP(z[t] - m);
                 l += z[t];
             }
             for (int c = 0; c < d; c++) {
-                double acc = 0.0;
+                acc_t acc = 0;
                 for (int i = 0; i < k; i++) {
                     const int blk = table[(size_t)r * k + i];
                     for (int t = 0; t < bs; t++)
@@ -463,19 +484,20 @@ int oracle_attention(int B, int Hq, int Hkv, int d, int bs, int k, int store_blo
  */
 int oracle_attention_masked(int B, int Hq, int Hkv, int d, int bs, int n_blocks, int store_blocks,
                             const void *q, int qdtype, const void *Ks, const void *Vs, int kvdtype,
-                            const uint8_t *mask, double scale, double *out)
+                            const uint8_t *mask, double scale, acc_t *out)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || bs <= 0 || n_blocks <= 0 ||
         store_blocks < n_blocks)
         return -1;
     const int G = Hq / Hkv;
     const int N = n_blocks * bs;
+    const acc_t sc = (acc_t)scale;
     int status = 0;
 #pragma omp parallel for schedule(dynamic) reduction(min : status)
     for (int64_t bh = 0; bh < (int64_t)B * Hq; bh++) {
         const int b = (int)(bh / Hq), h = (int)(bh % Hq), g = h / G;
         const int64_t r = (int64_t)b * Hkv + g;
-        double *z = malloc(sizeof(double) * (size_t)N);
+        acc_t *z = malloc(sizeof(acc_t) * (size_t)N);
         if (!z) {
             status = -2;
             continue;
@@ -486,12 +508,12 @@ int oracle_attention_masked(int B, int Hq, int Hkv, int d, int bs, int n_blocks,
                 continue;
             }
             const size_t kv = ((size_t)r * store_blocks * bs + t) * d;
-            double dot = 0.0;
+            acc_t dot = 0;
             for (int c = 0; c < d; c++)
                 dot += elem(q, qdtype, (size_t)bh * d + c) * elem(Ks, kvdtype, kv + c);
-            z[t] = scale * dot;
+            z[t] = sc * dot;
         }
-        double m = -INFINITY;
+        acc_t m = -INFINITY;
         for (int t = 0; t < N; t++)
             if (z[t] > m)
                 m = z[t];
@@ -500,13 +522,13 @@ int oracle_attention_masked(int B, int Hq, int Hkv, int d, int bs, int n_blocks,
             free(z);
             continue;
         }
-        double l = 0.0;
+        acc_t l = 0;
         for (int t = 0; t < N; t++) {
-            z[t] = exp(z[t] - m);   /* exp(-inf) = 0 outside the selection */
+            z[t] = ACC_EXP(z[t] - m);   /* exp(-inf) = 0 outside the selection */
             l += z[t];
         }
         for (int c = 0; c < d; c++) {
-            double acc = 0.0;
+            acc_t acc = 0;
             for (int t = 0; t < N; t++)
                 acc += z[t] * elem(Vs, kvdtype, ((size_t)r * store_blocks * bs + t) * d + c);
             out[(size_t)bh * d + c] = acc / l;

@@ -3,8 +3,11 @@
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check and by
 the benchmark's CPU-baseline leg.  The HIP product path never imports it.
 
-Every function takes NumPy arrays, widens nothing itself (the C code widens bf16
-bit patterns / float32 exactly to double) and returns float64 results.
+Two builds of the same C source exist.  The default ("f32") accumulates in float32 with
+sequential sums, the precision the oracle's contract names; it is the parity reference.  The
+"f64" build accumulates in double and serves to bound the f32 build's rounding.  Every function
+takes NumPy arrays, widens nothing itself (the C code widens bf16 bit patterns exactly) and
+returns arrays of its build's accumulator type; ``precision=`` picks the build per call.
 """
 
 from __future__ import annotations
@@ -18,34 +21,37 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nosa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_LIBS = {"f32": os.path.join(_HERE, "liboracle.so"), "f64": os.path.join(_HERE, "liboracle_f64.so")}
 
 F32, BF16, F64 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc + OpenMP (no HIP, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-               _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+    """Compile both builds of the oracle with gcc + OpenMP (no HIP, no fast-math); returns the
+    path of the default (f32) build."""
+    for prec, path in _LIBS.items():
+        if force or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            tmp = path + ".tmp%d" % os.getpid()
+            cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+                   *(["-DORACLE_F64"] if prec == "f64" else []), _SRC, "-o", tmp, "-lm"]
+            subprocess.run(cmd, check=True)
+            os.replace(tmp, path)
+    return _LIBS["f32"]
 
 
-_lib: Optional[ctypes.CDLL] = None
+_libs = {}
 
 
-def lib() -> ctypes.CDLL:
-    """The oracle library.  NOSA_ORACLE_LIBRARY names another build of the same source (the
-    mutation test points it at deliberately broken copies to show that the pins catch them)."""
-    global _lib
-    if _lib is None:
-        path = os.environ.get("NOSA_ORACLE_LIBRARY")
+def lib(precision: Optional[str] = None) -> ctypes.CDLL:
+    """The oracle library of one build ("f32", the default, or "f64").  NOSA_ORACLE_LIBRARY names
+    another build of the same source for the default (the mutation test points it at deliberately
+    broken copies to show that the pins catch them)."""
+    key = precision or "default"
+    if key not in _libs:
+        path = os.environ.get("NOSA_ORACLE_LIBRARY") if precision is None else None
         if not path:
-            path = _LIB
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            path = _LIBS[precision or "f32"]
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
                 build(force=True)
         L = ctypes.CDLL(path)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
@@ -60,8 +66,19 @@ def lib() -> ctypes.CDLL:
         L.oracle_locality.argtypes = [I64, I, I, P, P, P]
         L.oracle_set_threads.argtypes = [I]
         L.oracle_get_threads.restype = I
-        _lib = L
-    return _lib
+        L.oracle_acc_bits.restype = I
+        _libs[key] = L
+    return _libs[key]
+
+
+def acc_dtype(precision: Optional[str] = None):
+    """NumPy type of the accumulator of a build."""
+    return np.float64 if lib(precision).oracle_acc_bits() == 64 else np.float32
+
+
+def rounding_eps(precision: Optional[str] = None) -> float:
+    """Unit roundoff of a build's accumulator (2^-24 or 2^-53)."""
+    return float(np.finfo(acc_dtype(precision)).eps) / 2
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -84,55 +101,58 @@ def _check(rc: int, what: str) -> None:
         raise ValueError("oracle %s rejected its input (code %d)" % (what, rc))
 
 
-def set_threads(n: int) -> None:
-    lib().oracle_set_threads(int(n))
+def set_threads(n: int, precision: Optional[str] = None) -> None:
+    lib(precision).oracle_set_threads(int(n))
 
 
-def get_threads() -> int:
-    return int(lib().oracle_get_threads())
+def get_threads(precision: Optional[str] = None) -> int:
+    return int(lib(precision).oracle_get_threads())
 
 
-def pool_keys(k: np.ndarray, sbs: int, n_blocks: Optional[int] = None) -> np.ndarray:
-    """k: [B, Hkv, nb, bs, d] (bf16 bits / f32 / f64) -> Kp [B, Hkv, n_blocks*bs/sbs, d] float64."""
+def pool_keys(k: np.ndarray, sbs: int, n_blocks: Optional[int] = None, precision: Optional[str] = None) -> np.ndarray:
+    """k: [B, Hkv, nb, bs, d] (bf16 bits / f32 / f64) -> Kp [B, Hkv, n_blocks*bs/sbs, d]."""
     B, Hkv, nb, bs, d = k.shape
     if n_blocks is None:
         n_blocks = nb
     kk = np.ascontiguousarray(k[:, :, :n_blocks])
     n_tok = n_blocks * bs
-    out = np.empty((B, Hkv, n_tok // sbs, d), dtype=np.float64)
-    _check(lib().oracle_pool_keys(B * Hkv, n_tok, d, sbs, _ptr(kk), _dtype_code(kk), _ptr(out)), "pool_keys")
+    out = np.empty((B, Hkv, n_tok // sbs, d), dtype=acc_dtype(precision))
+    _check(lib(precision).oracle_pool_keys(B * Hkv, n_tok, d, sbs, _ptr(kk), _dtype_code(kk), _ptr(out)),
+           "pool_keys")
     return out
 
 
-def block_scores(q: np.ndarray, kp: np.ndarray, n_blocks: int, spb: int) -> np.ndarray:
-    """q: [B, Hq, d]; kp: [B, Hkv, nsub, d] float64 -> s [B, Hkv, n_blocks] float64."""
+def block_scores(q: np.ndarray, kp: np.ndarray, n_blocks: int, spb: int, precision: Optional[str] = None) -> np.ndarray:
+    """q: [B, Hq, d]; kp: [B, Hkv, nsub, d] (converted to the build's type) -> s [B, Hkv, n_blocks]."""
     B, Hq, d = q.shape
     _, Hkv, nsub, _ = kp.shape
+    at = acc_dtype(precision)
     q = np.ascontiguousarray(q)
-    kp = np.ascontiguousarray(kp, dtype=np.float64)
-    s = np.empty((B, Hkv, n_blocks), dtype=np.float64)
-    _check(lib().oracle_block_scores(B, Hq, Hkv, d, n_blocks, spb, _ptr(q), _dtype_code(q), _ptr(kp),
-                                     nsub, _ptr(s)), "block_scores")
+    kp = np.ascontiguousarray(kp, dtype=at)
+    s = np.empty((B, Hkv, n_blocks), dtype=at)
+    _check(lib(precision).oracle_block_scores(B, Hq, Hkv, d, n_blocks, spb, _ptr(q), _dtype_code(q), _ptr(kp),
+                                              nsub, _ptr(s)), "block_scores")
     return s
 
 
 def select(s: np.ndarray, evict: np.ndarray, kq: int, ke: int, n_prev: int = 0,
            agn_state: Optional[np.ndarray] = None, n_sink: int = 0,
-           n_window: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """s: [B, Hkv, n_blocks] float64; evict: [B, Hkv, >=n_blocks] float32.
+           n_window: int = 0, precision: Optional[str] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """s: [B, Hkv, n_blocks] block scores (converted to the build's type); evict: [B, Hkv, >=n_blocks]
+    float32.
 
     n_sink / n_window: blocks at the start / end of the visible context that always belong to
     the query-agnostic subset.  Returns (selected [B,Hkv,k] int32 ascending, agn_state
     [B,Hkv,ke] int32 ascending, is_agn [B,Hkv,k] bool)."""
     B, Hkv, n = s.shape
     k = kq + ke
-    s = np.ascontiguousarray(s, dtype=np.float64)
+    s = np.ascontiguousarray(s, dtype=acc_dtype(precision))
     ev = np.ascontiguousarray(evict, dtype=np.float32)
     st = np.zeros((B, Hkv, ke), dtype=np.int32) if agn_state is None else \
         np.ascontiguousarray(agn_state, dtype=np.int32).copy()
     sel = np.empty((B, Hkv, k), dtype=np.int32)
     isa = np.empty((B, Hkv, k), dtype=np.uint8)
-    _check(lib().oracle_select_sw(B * Hkv, n, kq, ke, n_sink, n_window, n_prev, _ptr(s), _ptr(ev), ev.shape[-1],
+    _check(lib(precision).oracle_select_sw(B * Hkv, n, kq, ke, n_sink, n_window, n_prev, _ptr(s), _ptr(ev), ev.shape[-1],
                                   _ptr(st) if ke > 0 else None, _ptr(sel), _ptr(isa)), "select")
     return sel, st, isa.astype(bool)
 
@@ -173,7 +193,7 @@ def gather(miss_cnt: np.ndarray, miss_list: np.ndarray, host: np.ndarray, cache:
 
 
 def attention(q: np.ndarray, k_store: np.ndarray, v_store: np.ndarray, table: np.ndarray,
-              scale: Optional[float] = None) -> np.ndarray:
+              scale: Optional[float] = None, precision: Optional[str] = None) -> np.ndarray:
     """Gather-form sparse attention. q: [B,Hq,d]; stores: [B,Hkv,nstore,bs,d]; table: [B,Hkv,k]."""
     B, Hq, d = q.shape
     _, Hkv, nstore, bs, _ = k_store.shape
@@ -185,14 +205,14 @@ def attention(q: np.ndarray, k_store: np.ndarray, v_store: np.ndarray, table: np
     ks = np.ascontiguousarray(k_store)
     vs = np.ascontiguousarray(v_store)
     tb = np.ascontiguousarray(table, dtype=np.int32)
-    out = np.empty((B, Hq, d), dtype=np.float64)
-    _check(lib().oracle_attention(B, Hq, Hkv, d, bs, k, nstore, _ptr(q), _dtype_code(q), _ptr(ks), _ptr(vs),
+    out = np.empty((B, Hq, d), dtype=acc_dtype(precision))
+    _check(lib(precision).oracle_attention(B, Hq, Hkv, d, bs, k, nstore, _ptr(q), _dtype_code(q), _ptr(ks), _ptr(vs),
                                   _dtype_code(ks), _ptr(tb), float(scale), _ptr(out)), "attention")
     return out
 
 
 def attention_masked(q: np.ndarray, k_store: np.ndarray, v_store: np.ndarray, mask: np.ndarray,
-                     scale: Optional[float] = None) -> np.ndarray:
+                     scale: Optional[float] = None, precision: Optional[str] = None) -> np.ndarray:
     """Masked-dense form. mask: [B, Hkv, n_blocks] (nonzero = attend the block)."""
     B, Hq, d = q.shape
     _, Hkv, nstore, bs, _ = k_store.shape
@@ -203,8 +223,8 @@ def attention_masked(q: np.ndarray, k_store: np.ndarray, v_store: np.ndarray, ma
     ks = np.ascontiguousarray(k_store)
     vs = np.ascontiguousarray(v_store)
     m = np.ascontiguousarray(mask, dtype=np.uint8)
-    out = np.empty((B, Hq, d), dtype=np.float64)
-    _check(lib().oracle_attention_masked(B, Hq, Hkv, d, bs, n_blocks, nstore, _ptr(q), _dtype_code(q), _ptr(ks),
+    out = np.empty((B, Hq, d), dtype=acc_dtype(precision))
+    _check(lib(precision).oracle_attention_masked(B, Hq, Hkv, d, bs, n_blocks, nstore, _ptr(q), _dtype_code(q), _ptr(ks),
                                          _ptr(vs), _dtype_code(ks), _ptr(m), float(scale), _ptr(out)),
            "attention_masked")
     return out
@@ -257,9 +277,10 @@ def locality(prev: np.ndarray, cur: np.ndarray, nbmax: int) -> np.ndarray:
 
 def decode_step(q: np.ndarray, kp: np.ndarray, evict: np.ndarray, k_store: np.ndarray, v_store: np.ndarray,
                 n_blocks: int, kq: int, ke: int, spb: int, n_prev: int = 0,
-                agn_state: Optional[np.ndarray] = None, n_sink: int = 0, n_window: int = 0) -> dict:
+                agn_state: Optional[np.ndarray] = None, n_sink: int = 0, n_window: int = 0,
+                precision: Optional[str] = None) -> dict:
     """One GPU-resident decode step in the pages' order: scores, selection, attention."""
-    s = block_scores(q, kp, n_blocks, spb)
-    sel, st, isa = select(s, evict, kq, ke, n_prev, agn_state, n_sink, n_window)
-    out = attention(q, k_store, v_store, sel)
+    s = block_scores(q, kp, n_blocks, spb, precision)
+    sel, st, isa = select(s, evict, kq, ke, n_prev, agn_state, n_sink, n_window, precision)
+    out = attention(q, k_store, v_store, sel, precision=precision)
     return {"scores": s, "selected": sel, "agn_state": st, "is_agn": isa, "out": out}

@@ -183,3 +183,30 @@ def test_rows_limit_rejected_on_host():
     with pytest.raises(N.NosaError) as ei:
         N.nosa_select(_good(batch=10000, n_kv_heads=8, n_q_heads=32), 16, 16, 16, 0, 16, 16, 256, stream=0)
     assert ei.value.code == N.NOSA_EUNSUPPORTED
+
+
+def test_decode_step_rejects_a_store_smaller_than_the_visible_blocks():
+    # Every selected id names a visible block, so a resident store of fewer blocks would let the
+    # kernels skip part of the selection: rejected on the host.
+    s = _good()
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_decode_step(s, 16, 16, 16, 0, 16, 16, 16, 16, 255, 0.1, 16, 256, stream=0)
+    assert ei.value.code == N.NOSA_EINVAL
+    assert "store_blocks" in N.nosa_last_error()
+
+
+def test_host_map_and_profile_hook_validate_on_host():
+    import ctypes
+    out = ctypes.c_void_p(123)
+    assert N.lib.nosa_host_map(None, ctypes.byref(out)) == N.NOSA_EINVAL
+    assert out.value is None
+    assert N.lib.nosa_host_map(16, None) == N.NOSA_EINVAL
+    # the profiling hook wants both events or neither
+    assert N.lib.nosa_profile_next_kernel(16, None) == N.NOSA_EINVAL
+    assert N.lib.nosa_profile_next_kernel(None, 16) == N.NOSA_EINVAL
+    assert N.lib.nosa_profile_next_kernel(None, None) == N.NOSA_OK
+    # an armed pair is consumed by the next decode call even when that call is rejected, so a
+    # failed call leaves nothing armed for a later one
+    assert N.lib.nosa_profile_next_kernel(16, 32) == N.NOSA_OK
+    with pytest.raises(N.NosaError):
+        N.nosa_decode_step(_good(), 16, 16, 16, 0, 16, 16, 16, 16, 0, 0.1, 16, 256, stream=0)

@@ -51,25 +51,78 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_src_sha256() != ha
 
 
-def test_traffic_record_needs_matching_code_and_workload(tmp_path, monkeypatch):
-    good = {"workload": "C2", "kernel_src_sha256": bench.kernel_src_sha256(), "bytes_per_launch": 123}
-    p = _write(tmp_path, "t.json", json.dumps(good))
-    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", {"C2": p})
-    assert bench.traffic_record("C2") == 123
-    assert bench.traffic_record("C3") is None                      # no record for that workload
-    _write(tmp_path, "t.json", json.dumps(dict(good, kernel_src_sha256="0" * 64)))
-    assert bench.traffic_record("C2") is None                      # taken on other kernel code
-    _write(tmp_path, "t.json", json.dumps(dict(good, workload="C3")))
-    assert bench.traffic_record("C2") is None                      # taken on another workload
+def test_kernel_bytes_of_each_plan():
+    # The dominant kernel of each plan of nosa_decode_step: the one-launch step moves the step's
+    # bytes; the attention launch with the pick inside also reads each row's block scores and
+    # query-agnostic ids and writes the selection; the two-call attention reads K/V, q and the ids.
+    for cfg in ("C2", "C3", "C5", "F1"):
+        w = WORKLOADS[cfg]
+        b = bench.algorithmic_bytes(w)
+        kv = w.rows * w.k * 64 * w.head_dim * 2 * 2
+        q = w.batch * w.n_q_heads * w.head_dim * 2
+        ids = w.rows * w.k * 4
+        assert b["kernel"]["row_step_kernel"] == b["step"]
+        assert b["kernel"]["step_decode_kernel"] == kv + q + w.rows * w.n_blocks * 4 + w.rows * w.ke * 4 + ids
+        assert b["kernel"]["decode_mfma_kernel"] == kv + q + ids
+    assert bench.algorithmic_bytes(WORKLOADS["C2"])["kernel"]["step_decode_kernel"] == 268746752
+
+
+def test_traffic_record_needs_matching_code_workload_and_kernel(tmp_path, monkeypatch):
+    good = {"workload": "C2", "kernel": "step_decode_kernel", "kernel_src_sha256": bench.kernel_src_sha256(),
+            "bytes_per_launch": 123}
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    p = bench.traffic_path("C2", "step_decode_kernel")
+    open(p, "w").write(json.dumps(good))
+    assert bench.traffic_record("C2", "step_decode_kernel") == 123
+    assert bench.traffic_record("C3", "step_decode_kernel") is None          # no record for that workload
+    assert bench.traffic_record("C2", "row_step_kernel") is None             # nor for that kernel
+    open(p, "w").write(json.dumps(dict(good, kernel_src_sha256="0" * 64)))
+    assert bench.traffic_record("C2", "step_decode_kernel") is None          # taken on other kernel code
+    open(p, "w").write(json.dumps(dict(good, workload="C3")))
+    assert bench.traffic_record("C2", "step_decode_kernel") is None          # names another workload
+
+
+def _counter_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for d, k, c, v in rows:
+            f.write('%d,"%s",%s,%s\n' % (d, k, c, v))
+
+
+def test_record_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkeypatch):
+    # FETCH_SIZE reads half of the copy's 256 MiB, WRITE_SIZE all of it: the factors are 2 and 1, and
+    # the kernel's per-dispatch means are scaled by them.
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    kib = 256 * 1024
+    _counter_csv(str(tmp_path / "f" / "x" / "pmc_counter_collection.csv"),
+                 [(1, "void nosa::step_decode_kernel<128, 4>(nosa::DecodeArgs)", "FETCH_SIZE", 100.0),
+                  (2, "void nosa::step_decode_kernel<128, 4>(nosa::DecodeArgs)", "FETCH_SIZE", 300.0),
+                  (3, "void nosa::combine_kernel<unsigned short, 128, 4>(nosa::DecodeArgs)", "FETCH_SIZE", 7.0)])
+    _counter_csv(str(tmp_path / "w" / "pmc_counter_collection.csv"),
+                 [(1, "void nosa::step_decode_kernel<128, 4>(nosa::DecodeArgs)", "WRITE_SIZE", 10.0)])
+    _counter_csv(str(tmp_path / "cf" / "cal_counter_collection.csv"),
+                 [(1, "void at::native::elementwise_kernel<128, 4>(int)", "FETCH_SIZE", kib / 2)])
+    _counter_csv(str(tmp_path / "cw" / "cal_counter_collection.csv"),
+                 [(1, "void at::native::elementwise_kernel<128, 4>(int)", "WRITE_SIZE", kib)])
+    bench.record_traffic("C2", "step_decode_kernel", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
+                         str(tmp_path / "cw"), ["cmd"])
+    rec = json.load(open(bench.traffic_path("C2", "step_decode_kernel")))
+    assert rec["raw_kib_per_dispatch"] == {"FETCH_SIZE": 200.0, "WRITE_SIZE": 10.0}
+    assert rec["fetch_bytes_per_launch"] == 200 * 1024 * 2 and rec["write_bytes_per_launch"] == 10 * 1024
+    assert rec["kernel_src_sha256"] == bench.kernel_src_sha256()
+    assert bench.traffic_record("C2", "step_decode_kernel") == 200 * 1024 * 2 + 10 * 1024
 
 
 def test_committed_traffic_records_are_close_to_the_algorithmic_bytes():
-    # Whatever code they were taken on, the committed counter records must describe the workload
-    # they name: measured HBM bytes within a few percent of the algorithmic bytes.
-    for cfg, key in (("C2", "decode"), ("C3", "step")):
-        rec = json.load(open(bench.PROFILE_TRAFFIC[cfg]))
-        assert rec["workload"] == cfg
-        alg = bench.algorithmic_bytes(WORKLOADS[cfg])[key]
+    # Whatever code they were taken on, the committed counter records must describe the workload and
+    # kernel they name: measured HBM bytes within a few percent of the algorithmic bytes.
+    import glob
+    recs = glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json"))
+    for path in recs:
+        rec = json.load(open(path))
+        assert os.path.basename(path) == "traffic_%s_%s.json" % (rec["kernel"], rec["workload"])
+        alg = bench.algorithmic_bytes(WORKLOADS[rec["workload"]])["kernel"][rec["kernel"]]
         assert rec["algorithmic_bytes_per_launch"] == alg
         assert alg <= rec["bytes_per_launch"] <= 1.03 * alg
 

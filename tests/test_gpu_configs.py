@@ -1,6 +1,7 @@
 """Full-size parity on the configured workloads, in the launch configuration the benchmark
-times (automatic splits and parts): C2 (B16, 16K ctx), C3 (B64, 4K ctx), C5 (B4, 128K ctx)
-end to end against the oracle element by element, and the C4 offload loop (128 steps, decode
+times (automatic splits and parts): C2 (B16, 16K ctx), C3 (B64, 4K ctx), C5 (B4, 128K ctx) and the
+sink + window split end to end against the oracle element by element, through the two calls and
+through nosa_decode_step (the call the benchmark times), and the C4 offload loop (128 steps, decode
 tokens appended through nosa_append_kv, the gather overlapped with attention by
 nosa_offload_decode on a copy stream) with per-step invariants and oracle checks on sampled
 steps."""
@@ -20,6 +21,7 @@ from tests import gpuhelp as H  # noqa: E402
 @pytest.mark.parametrize("cfg", ["C2", "C3", "C5", "F1"])
 def test_resident_config_end_to_end(cfg):
     w = WORKLOADS[cfg]
+    print("case", cfg, flush=True)
     x = generate(w)
     shape = H.shape_of(w)
     q_dev, k_dev, v_dev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"])
@@ -41,6 +43,46 @@ def test_resident_config_end_to_end(cfg):
     sel2, _ = H.gpu_select(shape, q_dev, kp, H.dev(x["evict"]), ws)
     out2 = H.gpu_decode(shape, q_dev, k_dev, v_dev, w.nbmax, sel2, ws)
     assert torch.equal(sel, sel2) and torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C5", "F1"])
+def test_decode_step_at_the_timed_shapes(cfg):
+    """nosa_decode_step, the call the benchmark times, in the benchmark's launch configuration
+    (automatic splits and parts) on the full workload: bs16/16K and the sink + window split take the
+    pick inside the attention launch (128 rows, two Gamma_e and two Gamma_q splits per row), bs64/4K
+    the one-launch step with its 64-block rows, bs4/128K its long-row plan.  Its selection must be
+    the oracle's (tie band) and bit-identical to nosa_select's, its output the oracle's attention
+    over that selection elementwise, and a repeat bit-identical."""
+    w = WORKLOADS[cfg]
+    print("case", cfg, flush=True)
+    x = generate(w)
+    shape = H.shape_of(w)
+    q_dev, k_dev, v_dev, ev_dev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
+    kp = H.gpu_pool(shape, k_dev)
+    ws = N.workspace(shape)
+    scale = 1.0 / np.sqrt(w.head_dim)
+
+    def step():
+        agn = torch.full((w.rows, w.ke), -7, dtype=torch.int32, device="cuda")
+        sel = torch.full((w.rows, w.k), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((w.batch, w.n_q_heads, w.head_dim), float("nan"), dtype=q_dev.dtype, device="cuda")
+        N.nosa_decode_step(shape, q_dev, kp, ev_dev, 0, agn, sel, k_dev, v_dev, w.nbmax, scale, out, ws)
+        return sel, agn, out
+
+    sel, agn, out = step()
+    sel_2c, agn_2c = H.gpu_select(shape, q_dev, kp, ev_dev, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel_2c) and torch.equal(agn[:, :w.ke], agn_2c[:, :w.ke])
+    s_ref = O.block_scores(x["q"], O.pool_keys(x["k"], 32), w.n_blocks, 2)
+    ties = H.check_selection(H.host(sel), H.host(agn), s_ref, x["evict"], w.kq, w.ke, n_sink=w.n_sink,
+                             n_window=w.n_window)
+    ref = O.attention(x["q"], x["k"], x["v"], H.host(sel).reshape(w.batch, w.n_kv_heads, w.k))
+    stats = H.check_attention(H.host(out), ref, w.dtype, cfg + " step")
+    print(cfg, "step: tie rows", ties, stats)
+    sel2, agn2, out2 = step()
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2) and torch.equal(agn, agn2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
 def test_c4_offload_loop():

@@ -608,3 +608,42 @@ def test_offload_decode_from_two_host_threads():
                 if a_.dtype == torch.bfloat16:
                     a_, b_ = a_.view(torch.int16), b_.view(torch.int16)
                 assert torch.equal(a_, b_), "thread %d differs from the loop run alone" % i
+
+
+@pytest.mark.parametrize("dtype,splits", [("bf16", 1), ("bf16", 4), ("f32", 1), ("f32", 3)])
+def test_sparse_decode_row_with_no_valid_block_gives_zero(dtype, splits):
+    # A row whose every table entry lies outside the store attends to no token: its output is 0
+    # (defined in the header; the oracle rejects such a table).  The other row is unaffected and
+    # matches the oracle over its valid entries.
+    w = small_workload("empty_row_" + dtype, batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=24, kq=6,
+                       ke=6, dtype=dtype, seed=38)
+    x = generate(w)
+    print("case", dtype, splits, flush=True)
+    shape = H.shape_of(w, decode_splits=splits)
+    table = np.tile(np.arange(12, dtype=np.int32) * 2, (2, 1))
+    table[0, :] = -1
+    table[0, 5] = w.nbmax            # past the store: skipped as well
+    ws = N.workspace(shape)
+    out = H.host(H.gpu_decode(shape, H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), w.nbmax, H.dev(table), ws))
+    torch.cuda.synchronize()
+    assert np.all(H.as_f64(out[:, 0:4]) == 0.0)
+    ref = O.attention(x["q"][:, 4:8].copy(), x["k"][:, 1:2].copy(), x["v"][:, 1:2].copy(), table[1].reshape(1, 1, -1))
+    H.check_attention(out[:, 4:8], ref, dtype, "valid row")
+
+
+def test_host_map_resolves_pinned_and_device_memory_and_rejects_pageable():
+    pinned = torch.empty(4096, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    assert N.host_map(dev) == dev.data_ptr()
+    addr = N.host_map(pinned)
+    assert addr != 0
+    # the mapped address is what the kernels read: a gather through it copies the pinned bytes
+    pinned.copy_(torch.arange(4096, dtype=torch.int32).to(torch.uint8))
+    su = torch.arange(16, dtype=torch.int32, device="cuda")
+    N.nosa_gather_units(addr, 256, dev, 256, 16, su, su, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(dev[:256].cpu(), pinned[:256])
+    pageable = np.zeros(4096, np.uint8)
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_host_map(pageable.ctypes.data)
+    assert ei.value.code == N.NOSA_EINVAL
