@@ -34,7 +34,7 @@ EXPORTED = (
     "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
     "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode", "nosa_offload_decode",
     "nosa_gather_units", "nosa_decode_step", "nosa_host_map", "nosa_profile_next_kernel",
-    "nosa_profile_last_kernel",
+    "nosa_profile_last_kernel", "nosa_decode_step_noalloc",
 )
 
 
@@ -111,6 +111,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_profile_next_kernel.argtypes = [P, P]
     L.nosa_profile_last_kernel.restype = ctypes.c_char_p
     L.nosa_profile_last_kernel.argtypes = []
+    L.nosa_decode_step_noalloc.restype = ctypes.c_int
+    L.nosa_decode_step_noalloc.argtypes = [SP, P, P, P, I32, P, P, P, P, I32, ctypes.c_float, P, P]
     return L
 
 
@@ -249,3 +251,11 @@ def nosa_decode_step(shape, q, pooled_k, evict, n_blocks_prev, agn_state, select
     _check(lib.nosa_decode_step(ctypes.byref(shape), _p(q), _p(pooled_k), _p(evict), int(n_blocks_prev),
                                 _p(agn_state), _p(selected), _p(k_store), _p(v_store), int(store_blocks),
                                 ctypes.c_float(softmax_scale), _p(out), _p(ws), _stream(stream)))
+
+
+def nosa_decode_step_noalloc(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, k_store, v_store,
+                             store_blocks, softmax_scale, out, stream=None) -> None:
+    """nosa_decode_step with the library's fixed per-GPU scratch as its workspace (allocates nothing)."""
+    _check(lib.nosa_decode_step_noalloc(ctypes.byref(shape), _p(q), _p(pooled_k), _p(evict), int(n_blocks_prev),
+                                        _p(agn_state), _p(selected), _p(k_store), _p(v_store), int(store_blocks),
+                                        ctypes.c_float(softmax_scale), _p(out), _stream(stream)))

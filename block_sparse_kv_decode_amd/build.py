@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnosa.so")
-SOURCES = ["api.cpp", "pool.hip", "select.hip", "cache.hip", "decode.hip"]
+SOURCES = ["api.cpp", "pool.hip", "select.hip", "cache.hip", "decode.hip", "noalloc.hip"]
 ARCH = os.environ.get("NOSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -236,6 +236,16 @@ struct ProfileMarks {
 
 }  // namespace
 
+namespace nosa {
+int api_fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+}  // namespace nosa
+
 extern "C" {
 
 const char *nosa_last_error(void) { return g_err; }

@@ -106,6 +106,9 @@ struct KernelMarks {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// Sets the calling thread's error message (nosa_last_error) and returns code.
+int api_fail(int code, const char *fmt, ...);
+
 // Each launcher returns hipSuccess or the error of the launch.
 hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_t st);
 hipError_t launch_append(int dtype, int d, const AppendArgs &a, int rows, hipStream_t st);

@@ -276,6 +276,26 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
                      hipStream_t stream);
 
 /*
+ * nosa_decode_step for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments and results are those of
+ * nosa_decode_step without `ws`: the step's workspace (block scores and split partials) is instead
+ * a fixed array of NOSA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from the
+ * library's load until the process ends.  The call allocates nothing.  Its first call on a device
+ * (with that device current) looks the array's device address up once (hipGetSymbolAddress); make
+ * that first call outside graph capture.  The array needs no initial contents and keeps whatever
+ * the last call left.  Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different host threads without ordering) race and give undefined
+ * results; order them, or use nosa_decode_step with a workspace per stream.
+ * Errors: those of nosa_decode_step, and NOSA_ECAPACITY when nosa_workspace_bytes(shape) exceeds
+ * NOSA_NOALLOC_SCRATCH_BYTES (checked on the host before any HIP call).
+ */
+#define NOSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int nosa_decode_step_noalloc(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                             int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, const void *k_store,
+                             const void *v_store, int32_t store_blocks, float softmax_scale, void *out,
+                             hipStream_t stream);
+
+/*
  * Transfer at a chosen granularity ([P1] §3.2: block-wise against element-wise communication;
  * [P1] §4: the transfer kernel reads pinned host memory through unified virtual addressing).
  * For u < n_units: bytes [src_unit[u] * unit_bytes, +unit_bytes) of src are copied to

@@ -210,3 +210,15 @@ def test_host_map_and_profile_hook_validate_on_host():
     assert N.lib.nosa_profile_next_kernel(16, 32) == N.NOSA_OK
     with pytest.raises(N.NosaError):
         N.nosa_decode_step(_good(), 16, 16, 16, 0, 16, 16, 16, 16, 0, 0.1, 16, 256, stream=0)
+
+
+def test_noalloc_step_validates_on_host():
+    # a shape whose workspace exceeds the fixed scratch, and an invalid shape, are both rejected
+    # before any HIP call
+    big = N.make_shape(batch=1024, n_q_heads=32, n_kv_heads=8, head_dim=128, n_blocks=2048, kq=32, ke=32)
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_decode_step_noalloc(big, 16, 16, 16, 0, 16, 16, 16, 16, 2048, 0.1, 16, stream=0)
+    assert ei.value.code == N.NOSA_ECAPACITY
+    with pytest.raises(N.NosaError) as ei:
+        N.nosa_decode_step_noalloc(_good(head_dim=96), 16, 16, 16, 0, 16, 16, 16, 16, 256, 0.1, 16, stream=0)
+    assert ei.value.code == N.NOSA_EUNSUPPORTED
