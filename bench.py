@@ -233,10 +233,23 @@ def run_resident(cfg, steps, warmup, want_events=True, decode_splits=0, select_p
     # timed region 1: the plain step loop (headline value): `warmup` untimed steps, then exactly
     # `steps` timed steps between two synchronisations
     wall_s = wall(step)
-    # the same region repeated (reported beside the headline, which stays the first region)
-    repeats = [1e3 * wall(step, warm=False) / steps for _ in range(3)]
+    # the same region repeated (reported beside the headline, which stays the first region), with
+    # events at both ends of each repeat: the GPU-side span shows how much of the wall time per step
+    # is host latency at the region's two ends
+    repeats, spans = [], []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        repeats.append(1e3 * (time.perf_counter() - t0) / steps)
+        spans.append(e0.elapsed_time(e1) / steps)
     res = {"wall_s": wall_s, "ms_per_step": 1e3 * wall_s / steps, "tokens_per_s": w.batch * steps / wall_s,
-           "ms_per_step_repeats": repeats, "layers": layers,
+           "ms_per_step_repeats": repeats, "gpu_span_ms_per_step_repeats": spans, "layers": layers,
            "ms_per_step_two_calls": 1e3 * wall(two_calls) / steps,
            "ms_per_step_steady": 1e3 * wall(steady) / steps}
     if want_events:
@@ -324,25 +337,28 @@ def check_step_outputs(cfg, res):
                 tie_band_rows=ties, seconds=round(time.perf_counter() - t0, 2), **stats)
 
 
-def run_offload(steps_cap=None):
-    """C4: 128-step offload loop (pinned host KV pool, 64-slot cache per KV head).
+def run_offload(cfg="C4", full=True, steps_cap=None):
+    """The 128-step offload loop of workload cfg (pinned host KV pool, 64-slot cache per KV head).
 
     A step appends the previous step's token (nosa_append_kv into the pinned host pool and the
-    pooled keys), selects, and runs nosa_offload_decode (gather on a copy stream, overlapped with
-    attention over the cache hits).  Every pass starts from the same state (empty cache, prompt
-    pooled keys): one pass records miss counts and selections, three timed passes run the
-    overlapped path and three the serial calls (cache_update on the compute stream, then
-    sparse_decode), with events only around steps 1..steps-1; a last serial pass with events
-    between the calls gives the per-phase breakdown and the gather rate."""
+    pooled keys; workloads with whole blocks arriving per step have them in the pool beforehand),
+    selects, and runs nosa_offload_decode (gather on a copy stream, overlapped with attention over
+    the cache hits).  Every pass starts from the same state (empty cache, prompt pooled keys): one
+    pass records miss counts, selections and query-agnostic subsets (for hit rate, bytes per step,
+    locality, and a check of the strict-eviction bounds), three timed passes run the overlapped path;
+    with `full`, three more run the serial calls (cache_update on the compute stream, then
+    sparse_decode), one serial pass with events between the calls gives the per-phase breakdown and
+    the gather rate, and the synchronised-step passes compare eager launches with HIP graphs."""
     import numpy as np
     import torch
 
     import block_sparse_kv_decode_amd as N
     from nosa_inputs import WORKLOADS, generate, visible_blocks
 
-    w = WORKLOADS["C4"]
+    w = WORKLOADS[cfg]
     x = generate(w)
     n0 = w.n_blocks
+    append = w.blocks_per_step == 0
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
@@ -353,23 +369,28 @@ def run_offload(steps_cap=None):
         t.copy_(src)
         return t
 
-    prompt_k, prompt_v = x["k"].copy(), x["v"].copy()
-    prompt_k[:, :, n0:] = 0
-    prompt_v[:, :, n0:] = 0
-    hk, hv = pin(prompt_k), pin(prompt_v)
-    del prompt_k, prompt_v
+    if append:   # the pool holds the prompt; the decode tokens are appended step by step
+        prompt_k, prompt_v = x["k"].copy(), x["v"].copy()
+        prompt_k[:, :, n0:] = 0
+        prompt_v[:, :, n0:] = 0
+        hk, hv = pin(prompt_k), pin(prompt_v)
+        del prompt_k, prompt_v
+    else:        # blocks arriving whole: written to the pool beforehand, made visible step by step
+        hk, hv = pin(x["k"]), pin(x["v"])
     hkd, hvd = N.host_map(hk), N.host_map(hv)     # the pool's device addresses, resolved once
     kdev = bf16(x["k"]).cuda()
     shape0 = N.make_shape(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
-                          n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, cache_slots=w.cache_slots)
+                          n_blocks=w.n_blocks, n_blocks_max=w.nbmax, kq=w.kq, ke=w.ke, cache_slots=w.cache_slots,
+                          sink_blocks=w.n_sink, window_blocks=w.n_window)
     R, k, C, d = w.rows, w.k, w.cache_slots, w.head_dim
     kp = torch.empty((R, w.nbmax * 2, d), dtype=torch.float32, device="cuda")
     acc = torch.empty((R, d), dtype=torch.float32, device="cuda")
-    # the decode tokens, step-major: token t of the decode is position n_tokens + t
-    new_k = bf16(x["k"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, d).transpose(2, 0, 1, 3)).cuda()
-    new_v = bf16(x["v"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, d).transpose(2, 0, 1, 3)).cuda()
-    positions = (torch.arange(w.steps, dtype=torch.int32, device="cuda").view(-1, 1) + (w.n_tokens - 1)) \
-        .expand(w.steps, w.batch).contiguous()
+    if append:
+        # the decode tokens, step-major: token t of the decode is position n_tokens + t
+        new_k = bf16(x["k"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, d).transpose(2, 0, 1, 3)).cuda()
+        new_v = bf16(x["v"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, d).transpose(2, 0, 1, 3)).cuda()
+        positions = (torch.arange(w.steps, dtype=torch.int32, device="cuda").view(-1, 1) + (w.n_tokens - 1)) \
+            .expand(w.steps, w.batch).contiguous()
     qs = bf16(x["q_steps"]).cuda()
     ev = torch.from_numpy(x["evict"]).cuda()
     del x
@@ -390,17 +411,20 @@ def run_offload(steps_cap=None):
     steps = w.steps if steps_cap is None else min(w.steps, steps_cap)
     mc_hist = torch.empty((steps, R), dtype=torch.int32, device="cuda")
     sel_hist = torch.empty((steps, R, k), dtype=torch.int32, device="cuda")
+    agn_hist = torch.empty((steps, R, w.ke), dtype=torch.int32, device="cuda")
 
     def reset():
         sob.fill_(-1)
         bos.fill_(-1)
-        N.nosa_pool_keys(shape0, kdev, 0, n0, kp)
+        # prompt blocks only when tokens are appended; every block otherwise (visibility limits use)
+        N.nosa_pool_keys(shape0, kdev, 0, n0 if append else w.nbmax, kp)
         torch.cuda.synchronize()
 
     def loop(overlap, timed=False, stats=False, phases=False):
         """One pass of the loop from the reset state.  timed: events only after step 0 and after
-        the last step (warm mean over steps 1..); stats: copies of miss counts and selections per
-        step; phases: events between the calls of every step (each event adds a few us)."""
+        the last step (warm mean over steps 1..); stats: copies of miss counts, selections and
+        query-agnostic subsets per step; phases: events between the calls of every step (each event
+        adds a few us)."""
         reset()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)] if phases else None
         ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -412,7 +436,7 @@ def run_offload(steps_cap=None):
             shape = shape0.copy(n_blocks=n)
             if phases:
                 evs[t][0].record(stream)
-            if t > 0:
+            if append and t > 0:
                 N.nosa_append_kv(shape0, new_k[t - 1], new_v[t - 1], positions[t], hkd, hvd, acc, kp, stream)
             N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
             if phases:
@@ -430,6 +454,7 @@ def run_offload(steps_cap=None):
             if stats:
                 mc_hist[t].copy_(mcnt)
                 sel_hist[t].copy_(sel)
+                agn_hist[t].copy_(agn)
             n_prev = n
         if timed:
             tb.record(stream)
@@ -446,7 +471,46 @@ def run_offload(steps_cap=None):
     loop(True, stats=True)                        # warm-up pass (code objects, host pool pages) + stats
     misses = mc_hist.sum(dim=1).cpu().numpy().tolist()
     s_h = sel_hist.cpu().numpy()
+    a_h = agn_hist.cpu().numpy()
     mean_ms = statistics.median([loop(True, timed=True)["warm_ms"] for _ in range(3)])
+    # Locality and the strict-eviction bounds, every row and step: the query-agnostic subset changes
+    # only by admitting arrivals (Gamma_e(t) within Gamma_e(t-1) and the arrivals A(t)), so adjacent
+    # selections share at least ke - a(t) blocks, a(t) = admitted arrivals; gamma >= (ke - a(t)) / k.
+    gam, bound, evicted = [], [], 0
+    for t in range(1, steps):
+        n_prev, n = visible_blocks(w, t - 1), visible_blocks(w, t)
+        for r in range(R):
+            E0, E1 = set(a_h[t - 1, r].tolist()), set(a_h[t, r].tolist())
+            arrivals = set(range(n_prev, n))
+            assert E1 <= E0 | arrivals, (cfg, t, r)
+            a_t = len(E1 & arrivals)
+            evicted += len(E0 - E1)
+            ov = len(set(s_h[t - 1, r].tolist()) & set(s_h[t, r].tolist()))
+            assert ov >= w.ke - a_t, (cfg, t, r, ov, a_t)
+            gam.append(ov / k)
+            bound.append((w.ke - a_t) / k)
+    warm = slice(1, steps)
+    blk_bytes = 64 * d * 2 * 2
+    fetched = [m * blk_bytes for m in misses]
+    res = {
+        "workload": "%s: B16, GQA 32/8, d128, 16K ctx (%s), %d+%d blocks%s, 64-slot GPU cache per KV head, %d steps" % (
+            cfg, "+1 token/step, appended to the pinned host pool" if append else
+            "+%d block(s) arriving per step" % w.blocks_per_step, w.kq, w.ke,
+            " (agnostic part incl. %d sink + %d window blocks)" % (w.n_sink, w.n_window) if w.n_window else "", steps),
+        "path": "%snosa_select + nosa_offload_decode (gather on a copy stream, overlapped with attention over the "
+                "hits)" % ("nosa_append_kv + " if append else ""),
+        "hit_rate_warm": 1.0 - statistics.mean(misses[warm]) / (R * k),
+        "fetched_bytes_per_step_warm": statistics.mean(fetched[warm]),
+        "cold_step_fetched_bytes": fetched[0],
+        "gamma_min": min(gam), "gamma_mean": statistics.mean(gam),
+        "gamma_guarantee_min": min(bound),
+        "agnostic_evictions_per_row_step": evicted / (R * (steps - 1)),
+        "strict_eviction_bounds_checked": True,
+        "step_ms_mean_warm": mean_ms,
+        "tokens_per_s": w.batch / (mean_ms * 1e-3),
+    }
+    if not full:
+        return res
     serial_ms = statistics.median([loop(False, timed=True)["warm_ms"] for _ in range(3)])
     ph = loop(False, phases=True)
     # A serving loop waits for every step.  Host wall time per step with a synchronisation after
@@ -466,14 +530,14 @@ def run_offload(steps_cap=None):
             n = visible_blocks(w, t)
             t0 = time.perf_counter()
             graphs.q.copy_(qs[t])
-            if t > 0:
+            if append and t > 0:
                 graphs.k_new.copy_(new_k[t - 1])
                 graphs.v_new.copy_(new_v[t - 1])
                 graphs.positions.copy_(positions[t])
             if use_graph:
-                graphs.replay(n, n_prev, t > 0)
+                graphs.replay(n, n_prev, append and t > 0)
             else:
-                graphs.enqueue(n, n_prev, t > 0)
+                graphs.enqueue(n, n_prev, append and t > 0)
             torch.cuda.synchronize()
             wall.append((time.perf_counter() - t0) * 1e3)
             n_prev = n
@@ -482,32 +546,17 @@ def run_offload(steps_cap=None):
     sync_loop(True)                               # captures the graphs
     sync_eager_ms = statistics.median([sync_loop(False) for _ in range(3)])
     sync_graph_ms = statistics.median([sync_loop(True) for _ in range(3)])
-    gam = []
-    for t in range(1, steps):
-        gam.extend(len(set(a.tolist()) & set(b.tolist())) / k for a, b in zip(s_h[t - 1], s_h[t]))
-    warm = slice(1, steps)
-    blk_bytes = 64 * d * 2 * 2
-    fetched = [m * blk_bytes for m in misses]
     cache_ms = statistics.mean(ph["cache"][warm])
-    return {
-        "workload": "C4: B16, GQA 32/8, d128, 16K ctx (+1 token/step, appended to the pinned host pool), 32+32 "
-                    "blocks, 64-slot GPU cache per KV head, %d steps" % steps,
-        "path": "nosa_append_kv + nosa_select + nosa_offload_decode (gather on a copy stream, overlapped with "
-                "attention over the hits)",
-        "hit_rate_warm": 1.0 - statistics.mean(misses[warm]) / (R * k),
-        "fetched_bytes_per_step_warm": statistics.mean(fetched[warm]),
-        "cold_step_fetched_bytes": fetched[0],
-        "gamma_min": min(gam) if gam else None, "gamma_mean": statistics.mean(gam) if gam else None,
-        "step_ms_mean_warm": mean_ms,
+    res.update({
         "serial_step_ms_mean_warm": serial_ms,
         "serial_phase_ms_mean_warm": {"append_select": statistics.mean(ph["select"][warm]),
                                       "cache_update": cache_ms, "sparse_decode": statistics.mean(ph["decode"][warm])},
         "h2d_gbps_warm_serial_cache_update": statistics.mean(fetched[warm]) / (cache_ms * 1e-3) / 1e9,
-        "tokens_per_s": w.batch / (mean_ms * 1e-3),
         "tokens_per_s_serial": w.batch / (serial_ms * 1e-3),
         "sync_every_step_wall_ms_median": {"eager": sync_eager_ms, "hip_graph": sync_graph_ms,
                                            "graphs_captured": len(graphs.graphs)},
-    }
+    })
+    return res
 
 
 def run_transfer(reps=20):
@@ -770,6 +819,7 @@ def main():
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": by["step"],
         "ms_per_step_repeats": main_res["ms_per_step_repeats"],
+        "gpu_span_ms_per_step_repeats": main_res["gpu_span_ms_per_step_repeats"],
         "ms_per_step_two_calls": main_res["ms_per_step_two_calls"],
         "ms_per_step_steady_state": main_res["ms_per_step_steady"],
         "step_ms_median_events": main_res["step_ms_median"],
@@ -791,6 +841,7 @@ def main():
         also[cfg] = {
             "workload": describe(r["workload"]), "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
             "ms_per_step_repeats": r["ms_per_step_repeats"],
+            "gpu_span_ms_per_step_repeats": r["gpu_span_ms_per_step_repeats"],
             "ms_per_step_two_calls": r["ms_per_step_two_calls"],
             "ms_per_step_steady_state": r["ms_per_step_steady"],
             "step_hbm_gbps": b2["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
@@ -804,9 +855,11 @@ def main():
         line["also"] = also
     link = None
     if not args.no_offload:
-        line["offload"] = run_offload()
+        line["offload"] = run_offload("C4")
         link = measure_link_peak()
         line["offload"]["link_peak_gbps_sdma"] = link
+        # the eviction dynamics: one block arriving per step, and the pages' 16 + 48 split
+        line["offload"]["variants"] = {cfg: run_offload(cfg, full=False) for cfg in ("C4S", "C4P", "C4PS")}
     if not args.no_transfer:
         line["transfer_granularity"] = run_transfer()
         line["transfer_granularity"]["link_peak_gbps_sdma"] = link if link is not None else measure_link_peak()

@@ -73,6 +73,8 @@ class Workload:
     drift_sigma: float = 0.0          # std of the per-step query drift (offload loop only)
     n_sink: int = 0                   # first blocks always in the query-agnostic subset
     n_window: int = 0                 # most recent blocks always in the query-agnostic subset
+    blocks_per_step: int = 0          # offload loop: 0 = one token per step (appended); b > 0 = b whole
+                                      # blocks become visible per step (written to the pool beforehand)
     description: str = ""
 
     @property
@@ -111,6 +113,18 @@ WORKLOADS: Dict[str, Workload] = {
     # query-agnostic ones that include 1 sink block and a 16-block sliding window.
     "F1": Workload("F1", 16, 32, 8, 128, 16384, 16, 48, "bf16", seed=2, n_sink=1, n_window=16,
                    description="C2 tensors with the paper split: 16 query-aware + 48 agnostic (1 sink, 16 window)"),
+    # The offload loop with the paper's split (the C4 tensors): the window slides as blocks fill.
+    "C4P": Workload("C4P", 16, 32, 8, 128, 16384, 16, 48, "bf16", seed=4, n_blocks_max=258, cache_slots=64,
+                    steps=128, drift_sigma=0.3, n_sink=1, n_window=16,
+                    description="offload loop, paper split 16 + 48 (1 sink, 16 window), 1 token per step"),
+    # Stress variants: one whole block arrives at every step (blocks 256 .. 382 become visible at
+    # steps 1 .. 127), so the query-agnostic subset drops its lowest member (or the arrival) every step.
+    "C4S": Workload("C4S", 16, 32, 8, 128, 16384, 32, 32, "bf16", seed=6, n_blocks_max=383, cache_slots=64,
+                    steps=128, drift_sigma=0.3, blocks_per_step=1,
+                    description="offload loop, 32 + 32, one block arriving per step"),
+    "C4PS": Workload("C4PS", 16, 32, 8, 128, 16384, 16, 48, "bf16", seed=6, n_blocks_max=383, cache_slots=64,
+                     steps=128, drift_sigma=0.3, n_sink=1, n_window=16, blocks_per_step=1,
+                     description="offload loop, paper split 16 + 48 (1 sink, 16 window), one block per step"),
 }
 
 
@@ -167,11 +181,14 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
 
 
 def visible_blocks(w: Workload, step: int) -> int:
-    """Blocks fully written at decode step ``step`` when one token is appended per step.
+    """Blocks visible at decode step ``step``.
 
-    The context holds ``n_tokens + step`` tokens at step ``step``; only whole blocks are
-    visible to selection and attention.
+    One token appended per step (blocks_per_step = 0): the context holds ``n_tokens + step``
+    tokens at step ``step``, and only whole blocks are visible to selection and attention.
+    Otherwise ``blocks_per_step`` whole blocks join the visible context at every step.
     """
+    if w.blocks_per_step:
+        return min(w.nbmax, w.n_tokens // BLOCK + step * w.blocks_per_step)
     return min(w.nbmax, (w.n_tokens + step) // BLOCK)
 
 

@@ -85,21 +85,32 @@ def test_decode_step_at_the_timed_shapes(cfg):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-def test_c4_offload_loop():
-    w = WORKLOADS["C4"]
+@pytest.mark.parametrize("cfg", ["C4", "C4P", "C4S", "C4PS"])
+def test_c4_offload_loop(cfg):
+    """The 128-step offload loop: C4 (32 + 32, one token per step), C4P (the pages' 16 + 48 split with
+    1 sink and a 16-block window), and the stress variants C4S / C4PS (one whole block arriving per
+    step, so that the query-agnostic subset drops its lowest member or the arrival every step)."""
+    w = WORKLOADS[cfg]
+    print("case", cfg, flush=True)
     x = generate(w)
     shape0 = H.shape_of(w)
     R, k, C = w.rows, w.k, w.cache_slots
     n0 = w.n_blocks
-    # The host pool and the pooled keys start with the prompt; the decode tokens join them through
-    # nosa_append_kv, one per step.
-    prompt_k, prompt_v = x["k"].copy(), x["v"].copy()
-    prompt_k[:, :, n0:] = 0
-    prompt_v[:, :, n0:] = 0
-    hk, hv = H.pinned(prompt_k), H.pinned(prompt_v)
-    del prompt_k, prompt_v
+    append = w.blocks_per_step == 0
+    if append:
+        # The host pool and the pooled keys start with the prompt; the decode tokens join them
+        # through nosa_append_kv, one per step.
+        prompt_k, prompt_v = x["k"].copy(), x["v"].copy()
+        prompt_k[:, :, n0:] = 0
+        prompt_v[:, :, n0:] = 0
+        hk, hv = H.pinned(prompt_k), H.pinned(prompt_v)
+        del prompt_k, prompt_v
+    else:
+        # whole blocks arrive: the pool holds them beforehand, and visibility grows a block per step
+        hk, hv = H.pinned(x["k"]), H.pinned(x["v"])
+    hkd, hvd = N.host_map(hk), N.host_map(hv)
     kp = torch.full((R, w.nbmax * 2, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
-    N.nosa_pool_keys(shape0, H.dev(x["k"]), 0, n0, kp)      # reads blocks [0, n0) only
+    N.nosa_pool_keys(shape0, H.dev(x["k"]), 0, n0 if append else w.nbmax, kp)
     acc = torch.zeros((R, w.head_dim), dtype=torch.float32, device="cuda")
     kn_all = H.dev(np.ascontiguousarray(x["k"][:, :, n0:].reshape(w.batch, w.n_kv_heads, -1, w.head_dim)
                                          .transpose(2, 0, 1, 3)))
@@ -131,14 +142,14 @@ def test_c4_offload_loop():
             torch.cuda.synchronize()
             snap = {"agn": None if agn is None else H.host(agn).copy(), "sob": H.host(sob).copy(),
                     "bos": H.host(bos).copy()}
-        if t > 0:
+        if append and t > 0:
             pos = w.n_tokens + t - 1
             N.nosa_append_kv(shape0, kn_all[t - 1], vn_all[t - 1],
-                             torch.full((w.batch,), pos, dtype=torch.int32, device="cuda"), hk, hv, acc, kp)
+                             torch.full((w.batch,), pos, dtype=torch.int32, device="cuda"), hkd, hvd, acc, kp)
         q_t = q_all[t]
         sel, agn = H.gpu_select(shape, q_t, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
         out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-        N.nosa_offload_decode(shape, q_t, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out, ws,
+        N.nosa_offload_decode(shape, q_t, sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, scale, out, ws,
                               copy=copy_stream)
         torch.cuda.synchronize()
         sel_h = H.host(sel)
@@ -146,7 +157,11 @@ def test_c4_offload_loop():
         assert np.all(np.diff(sel_h, axis=1) > 0) and sel_h.min() >= 0 and sel_h.max() < n
         if prev_sel is not None:
             gam = O.locality(prev_sel, sel_h, w.nbmax)
-            admitted = np.array([len(set(H.host(agn)[r].tolist()) & set(range(n_prev, n))) for r in range(R)])
+            agn_h = H.host(agn)
+            admitted = np.array([len(set(agn_h[r].tolist()) & set(range(n_prev, n))) for r in range(R)])
+            # strict eviction: Gamma_e(t) within Gamma_e(t-1) and the arrivals, so the overlap bound
+            for r in range(R):
+                assert set(agn_h[r].tolist()) <= set(prev_agn[r].tolist()) | set(range(n_prev, n))
             assert np.all(gam >= (w.ke - admitted) / k - 1e-12)
             # cache = budget: the cache after step t-1 holds exactly Gamma(t-1), so hits = k * gamma
             assert np.array_equal(k - mc, np.rint(k * gam).astype(np.int32))
@@ -157,7 +172,8 @@ def test_c4_offload_loop():
                 kp_ref = O.pool_keys(x["k"], 32)
             s_ref = O.block_scores(x["q_steps"][t], kp_ref[:, :, :2 * n], n, 2)
             H.check_selection(sel_h, H.host(agn), s_ref, x["evict"], w.kq, w.ke, n_prev,
-                              None if snap["agn"] is None else snap["agn"].reshape(w.batch, w.n_kv_heads, w.ke))
+                              None if snap["agn"] is None else snap["agn"].reshape(w.batch, w.n_kv_heads, w.ke),
+                              n_sink=w.n_sink, n_window=w.n_window)
             sob_ref, bos_ref = snap["sob"], snap["bos"]
             tab_ref, mc_ref, ml_ref = O.cache_step(sel_h, sob_ref, bos_ref)
             assert np.array_equal(H.host(sob), sob_ref) and np.array_equal(H.host(bos), bos_ref)
@@ -173,14 +189,17 @@ def test_c4_offload_loop():
                         assert np.array_equal(ckh[b, g, s_], x["k"][b, g, blk])
                         assert np.array_equal(cvh[b, g, s_], x["v"][b, g, blk])
         prev_sel = sel_h
+        prev_agn = H.host(agn).copy()
         n_prev = n
         if t % 32 == 0:
             print("C4 step %d ok" % t, flush=True)
-    # pooled keys built by the appends: bit-identical to pooling the full store at once
-    torch.cuda.synchronize()
-    n_end = visible_blocks(w, w.steps - 1)
-    kp_once = H.gpu_pool(shape0, H.dev(x["k"]))
-    assert torch.equal(kp[:, :2 * n_end].view(torch.int32), kp_once[:, :2 * n_end].view(torch.int32))
+    if append:
+        # pooled keys built by the appends: bit-identical to pooling the full store at once
+        torch.cuda.synchronize()
+        n_end = visible_blocks(w, w.steps - 1)
+        kp_once = H.gpu_pool(shape0, H.dev(x["k"]))
+        assert torch.equal(kp[:, :2 * n_end].view(torch.int32), kp_once[:, :2 * n_end].view(torch.int32))
     g = np.concatenate(gammas)
-    print("C4 gamma min %.3f mean %.3f; hit rate (warm) %.3f" % (g.min(), g.mean(), np.mean(hits[1:]) / k))
-    assert g.min() >= w.ke / k - 1e-12
+    print("%s gamma min %.3f mean %.3f; hit rate (warm) %.3f" % (cfg, g.min(), g.mean(), np.mean(hits[1:]) / k))
+    # at most one block arrives per step in every variant, so locality never drops below (ke - 1) / k
+    assert g.min() >= (w.ke - 1) / k - 1e-12

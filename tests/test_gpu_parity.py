@@ -301,10 +301,12 @@ def test_c1_tiny_end_to_end():
 
 
 @pytest.mark.parametrize("n,kq,ke,parts", [(513, 16, 16, 0), (1300, 40, 24, 3), (1300, 40, 24, 1), (2048, 32, 32, 0),
-                                           (5000, 32, 32, 7), (700, 300, 100, 0), (4100, 20, 30, 1)])
+                                           (5000, 32, 32, 7), (700, 300, 100, 0), (4100, 20, 30, 1),
+                                           (3000, 8, 8, 5), (1500, 10, 90, 4), (2040, 64, 0, 7)])
 def test_select_long_rows(n, kq, ke, parts):
     # Rows longer than 512 blocks take the bounded-candidate top-k; the next step (blocks arrive,
-    # strict eviction) runs the same path with few query-agnostic candidates.
+    # strict eviction) runs the same path with few query-agnostic candidates.  The cases cover one
+    # to a few long scoring slices, a budget of 100 with 90 query-agnostic blocks, and ke = 0.
     rng = np.random.default_rng(n)
     B, Hkv, G, d = 2, 2, 4, 128
     nbmax = n + 9
@@ -324,6 +326,24 @@ def test_select_long_rows(n, kq, ke, parts):
     sel2, agn2 = H.gpu_select(shape2, q_dev, kp_dev, ev_dev, ws, n_prev=n, agn=agn)
     s_ref2 = O.block_scores(q, kp.astype(np.float64), n2, 2)
     H.check_selection(H.host(sel2), H.host(agn2), s_ref2, ev, kq, ke, n, agn_ref)
+
+
+def test_select_long_rows_exact_ties_go_to_lower_ids():
+    # Integer-valued pooled keys and eviction scores make many keys exactly equal; with five scoring
+    # slices of 600 blocks, ties must go to the lower block id in both subsets, exactly as in the
+    # oracle.
+    rng = np.random.default_rng(77)
+    B, Hkv, G, d, n, kq, ke, parts = 2, 2, 2, 64, 3000, 6, 10, 5
+    q = np.ones((B, Hkv * G, d), np.float32)
+    kp = rng.integers(0, 2, size=(B, Hkv, n * 2, d)).astype(np.float32)
+    ev = rng.integers(0, 3, size=(B, Hkv, n)).astype(np.float32)
+    shape = N.make_shape(batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=d, n_blocks=n, kq=kq, ke=ke,
+                         dtype=N.NOSA_F32, select_parts=parts)
+    sel, agn = H.gpu_select(shape, H.dev(q), H.dev(kp), H.dev(ev), N.workspace(shape))
+    s_ref = O.block_scores(q, kp, n, 2)
+    sel_o, agn_o, _ = O.select(s_ref, ev, kq, ke)
+    assert np.array_equal(H.host(agn).reshape(B, Hkv, ke), agn_o)
+    assert np.array_equal(H.host(sel).reshape(B, Hkv, kq + ke), sel_o)
 
 
 def test_select_long_rows_all_ties():
