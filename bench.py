@@ -683,9 +683,9 @@ def traffic_record(cfg, kernel):
     return rec.get("bytes_per_launch")
 
 
-def _counter_kib(csv_dir, counter, kernel):
-    """Mean value of `counter` per dispatch of the kernels whose name starts with `kernel`, from the
-    counter_collection CSV files rocprofv3 wrote under csv_dir."""
+def _counter_kib(csv_dir, counter, kernel, contains=""):
+    """Mean value of `counter` per dispatch of the kernels whose base name is `kernel` (and whose full
+    name contains `contains`), from the counter_collection CSV files rocprofv3 wrote under csv_dir."""
     import csv
     import glob
     vals = {}
@@ -693,7 +693,7 @@ def _counter_kib(csv_dir, counter, kernel):
         for row in csv.DictReader(open(f)):
             name = row.get("Kernel_Name", "")
             base = name.split("(")[0].split("<")[0].split(" ")[-1].split("::")[-1]
-            if row.get("Counter_Name") == counter and base == kernel:
+            if row.get("Counter_Name") == counter and base == kernel and contains in name:
                 key = (f, row.get("Dispatch_Id"))
                 vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
     if not vals:
@@ -708,8 +708,9 @@ def record_traffic(cfg, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_write_d
     from nosa_inputs import WORKLOADS
     fk, nf = _counter_kib(fetch_dir, "FETCH_SIZE", kernel)
     wk, nw = _counter_kib(write_dir, "WRITE_SIZE", kernel)
-    cf, _ = _counter_kib(cal_fetch_dir, "FETCH_SIZE", "elementwise_kernel")
-    cw, _ = _counter_kib(cal_write_dir, "WRITE_SIZE", "elementwise_kernel")
+    # the copy: torch's elementwise multiply by 1 (the tensor fill before it is another kernel)
+    cf, _ = _counter_kib(cal_fetch_dir, "FETCH_SIZE", "vectorized_elementwise_kernel", "MulFunctor")
+    cw, _ = _counter_kib(cal_write_dir, "WRITE_SIZE", "vectorized_elementwise_kernel", "MulFunctor")
     true_kib = (64 << 20) * 4 / 1024.0
     ff, wf = true_kib / cf, true_kib / cw
     fetch_b, write_b = fk * 1024 * ff, wk * 1024 * wf

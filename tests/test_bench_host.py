@@ -101,10 +101,14 @@ def test_record_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkey
                   (3, "void nosa::combine_kernel<unsigned short, 128, 4>(nosa::DecodeArgs)", "FETCH_SIZE", 7.0)])
     _counter_csv(str(tmp_path / "w" / "pmc_counter_collection.csv"),
                  [(1, "void nosa::step_decode_kernel<128, 4>(nosa::DecodeArgs)", "WRITE_SIZE", 10.0)])
+    mul = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, float, " \
+          "at::native::binary_internal::MulFunctor<float> >, std::array<char*, 2ul> >(int)"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>, " \
+           "std::array<char*, 1ul> >(int)"
     _counter_csv(str(tmp_path / "cf" / "cal_counter_collection.csv"),
-                 [(1, "void at::native::elementwise_kernel<128, 4>(int)", "FETCH_SIZE", kib / 2)])
+                 [(1, fill, "FETCH_SIZE", 17.0), (2, mul, "FETCH_SIZE", kib / 2)])
     _counter_csv(str(tmp_path / "cw" / "cal_counter_collection.csv"),
-                 [(1, "void at::native::elementwise_kernel<128, 4>(int)", "WRITE_SIZE", kib)])
+                 [(1, fill, "WRITE_SIZE", kib), (2, mul, "WRITE_SIZE", kib)])
     bench.record_traffic("C2", "step_decode_kernel", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
                          str(tmp_path / "cw"), ["cmd"])
     rec = json.load(open(bench.traffic_path("C2", "step_decode_kernel")))
