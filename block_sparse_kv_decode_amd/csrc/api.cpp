@@ -49,11 +49,14 @@ constexpr int kMinBlocksPerPart = 8;
 // A split shorter than this many blocks spends more time filling its load pipeline and merging
 // than it saves (measured on MI355X: 4-block splits lose to 8-block splits at 128K context).
 constexpr int kMinBlocksPerSplit = 8;
-// Rows up to this many blocks run the fused decode step: their Gamma_q ranking in a 256-thread
-// workgroup is a single pass.  Longer rows rank more slowly there than the attention splits can
-// hide (measured on MI355X at 2048 blocks per row and 32 rows: 49.4 us per step fused vs 46.2 us
-// in two calls).
+// Rows the fused decode step takes: their Gamma_q ranking in a 256-thread workgroup must hide under
+// the Gamma_e splits' streaming.  Up to 512 blocks the LDS ranking does; up to 2048 blocks (8 per
+// thread) with both subsets of at most 64 blocks, the ranking from registers does.
 constexpr int kStepMaxBlocks = 512;
+constexpr int kStepRegMaxBlocks = 2048;
+bool step_rows_fit(const nosa_shape *s) {
+    return s->n_blocks <= kStepMaxBlocks || (s->n_blocks <= kStepRegMaxBlocks && s->kq <= 64 && s->ke <= 64);
+}
 
 int check_shape(const nosa_shape *s) {
     if (!s) return fail(NOSA_EINVAL, "shape is NULL");
@@ -611,8 +614,7 @@ int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled
     const SplitPlan dp = decode_plan(shape);
     // The pick moves into the attention launch when the selection would otherwise need its own
     // Gamma_q kernel (multi-part plan), for bf16 rows with both subsets non-empty.
-    const bool fused = shape->dtype == NOSA_BF16 && pp.P > 1 && shape->kq > 0 && shape->ke > 0 &&
-                       shape->n_blocks <= kStepMaxBlocks;
+    const bool fused = shape->dtype == NOSA_BF16 && pp.P > 1 && shape->kq > 0 && shape->ke > 0 && step_rows_fit(shape);
     // One workgroup per row does it all when it would both score-and-select the row and attend it
     // in a single split anyway.
     const bool row_fused = shape->dtype == NOSA_BF16 && pp.P == 1 && pp.threads == 256 && dp.S == 1 &&

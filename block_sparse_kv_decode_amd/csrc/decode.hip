@@ -570,34 +570,41 @@ __global__ __launch_bounds__(256, 2) void step_decode_kernel(DecodeArgs a, Selec
     const RowLds L = carve<256>(dyn, n);
     int32_t *qlist = (int32_t *)(dyn + row_lds_bytes<256>(n));   // [kq] Gamma_q, ascending
     const float *gscore = s.scores + (size_t)row * s.scores_stride;
-    // Gamma_e ids loaded together with the scores (one memory round trip), marked after the clear
-    constexpr int kAgnPer = 2;   // ids per thread in flight; more are read after the barrier
-    int ids[kAgnPer];
-#pragma unroll
-    for (int r = 0; r < kAgnPer; ++r) {
-        const int j = tid + r * 256;
-        ids[r] = j < s.ke ? s.agn[(size_t)row * s.ke + j] : -1;
-    }
-    scores_to_lds<256>(gscore, n, L);
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kAgnPer; ++r)
-        if (ids[r] >= 0 && ids[r] < n) L.inE[ids[r]] = 1;
-    for (int j = tid + kAgnPer * 256; j < s.ke; j += 256) {
-        const int id = s.agn[(size_t)row * s.ke + j];
-        if (id >= 0 && id < n) L.inE[id] = 1;
-    }
-    __syncthreads();
+    const int32_t *agn = s.agn + (size_t)row * s.ke;
+    const int k = s.kq + s.ke;
+    // the first Gamma_q split writes the row's selection
+    int32_t *selrow = sp == S_e ? s.sel + (size_t)row * k : nullptr;
     // The ranking shares its CU with streaming attention workgroups: give it issue priority.
     __builtin_amdgcn_s_setprio(2);
-    topk_mark<256>(
-        n, s.kq, [&](int i) { return order_key(L.sc[i]); }, [&](int i) { return !L.inE[i]; }, L.inQ, L.keys, ssh);
-    const int k = s.kq + s.ke;
-    // one pass: Gamma_q (ascending) into LDS, and the first Gamma_q split writes the selection
-    compact_outputs<256>(n, L.inQ, L.inE, qlist, s.kq, sp == S_e ? s.sel + (size_t)row * k : nullptr,
-                         sp == S_e ? k : 0, ssh);
+    if (!reg_pick_fits<256>(n, s.kq, s.ke) ||
+        !pick_query_regs<256>(gscore, n, agn, s.ke, s.kq, L.keys, qlist, selrow, ssh)) {
+        // Gamma_e ids loaded together with the scores (one memory round trip), marked after the clear
+        constexpr int kAgnPer = 2;   // ids per thread in flight; more are read after the barrier
+        int ids[kAgnPer];
+#pragma unroll
+        for (int r = 0; r < kAgnPer; ++r) {
+            const int j = tid + r * 256;
+            ids[r] = j < s.ke ? agn[j] : -1;
+        }
+        scores_to_lds<256>(gscore, n, L);
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kAgnPer; ++r)
+            if (ids[r] >= 0 && ids[r] < n) L.inE[ids[r]] = 1;
+        for (int j = tid + kAgnPer * 256; j < s.ke; j += 256) {
+            const int id = agn[j];
+            if (id >= 0 && id < n) L.inE[id] = 1;
+        }
+        __syncthreads();
+        topk_mark<256>(
+            n, s.kq, [&](int i) { return order_key(L.sc[i]); }, [&](int i) { return !L.inE[i]; }, L.inQ, L.keys,
+            ssh);
+        // one pass: Gamma_q (ascending) into LDS, and the selection
+        compact_outputs<256>(n, L.inQ, L.inE, qlist, s.kq, selrow, selrow ? k : 0, ssh);
+    }
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();
+    // qlist complete in LDS; the selection's global stores need not have landed
+    wg_barrier();
     const int j0 = (sp - S_e) * a.nbs, j1 = min(s.kq, j0 + a.nbs);
     decode_mfma_split<D, G>(a, row, sp, qlist, 1, j0, j1, sh, nullptr, &qf);
 }

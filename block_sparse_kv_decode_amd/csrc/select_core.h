@@ -265,6 +265,204 @@ __device__ void compact_outputs(int n, const uint8_t *inE, const uint8_t *inQ, i
         for (int p = ne + tid; p < ke; p += NT) agn[p] = -1;
 }
 
+// ---- Gamma_q of a row held in registers ------------------------------------------------------
+// For rows of at most kRegPickMax * NT (= 2048) blocks and both subsets of at most 64 blocks.
+// Thread t owns the kpt consecutive blocks [t * kpt, t * kpt + kpt), kpt the smallest power of two
+// with kpt * NT >= n, and builds their keys in registers straight from the scores in global memory:
+// same keys, candidates and tie order as topk_mark, and the same chunk-maximum bound, with chunks of
+// up to four threads (at most 64 of them).  The steps work on whole waves with lane ballots rather
+// than on per-key counts, and take two workgroup barriers (three with more than 64 survivors):
+//   - each wave marks Gamma_e in an LDS bitmap of its own and reads its threads' bits;
+//   - after the chunk maxima are in LDS, every wave finds their kq-th best, T0, by a most-significant-
+//     bit-first search on ballots (one maximum per lane);
+//   - survivors (keys >= T0) are placed with ballots and one LDS atomic per wave;
+//   - after the survivors are in LDS, wave 0 takes their kq-th best the same way (one survivor per
+//     lane), so the winners are the survivors at or above it, and orders ids through an LDS bitmap
+//     of the row with prefix popcounts: Gamma_q ascending into qlist and, when sel is given, the
+//     ascending union with Gamma_e into sel.
+// The loads are issued unconditionally (indices clamped into the row), Gamma_e ids first, so that
+// waiting for the ids waits for nothing else.
+constexpr int kRegPickMax = 8;
+
+template <int NT>
+__host__ __device__ inline bool reg_pick_fits(int n, int kq, int ke) {
+    return n >= 1 && n <= kRegPickMax * NT && n <= 2048 && kq >= 1 && kq <= 64 && ke <= 64;
+}
+
+__device__ __forceinline__ uint64_t dpp_max64(uint64_t v, int ctrl_is_xor2) {
+    const int lo = (int)(uint32_t)v, hi = (int)(v >> 32);
+    const int olo = ctrl_is_xor2 ? __builtin_amdgcn_update_dpp(0, lo, kDppQuadXor2, 0xF, 0xF, false)
+                                 : __builtin_amdgcn_update_dpp(0, lo, kDppQuadXor1, 0xF, 0xF, false);
+    const int ohi = ctrl_is_xor2 ? __builtin_amdgcn_update_dpp(0, hi, kDppQuadXor2, 0xF, 0xF, false)
+                                 : __builtin_amdgcn_update_dpp(0, hi, kDppQuadXor1, 0xF, 0xF, false);
+    const uint64_t o = ((uint64_t)(uint32_t)ohi << 32) | (uint32_t)olo;
+    return o > v ? o : v;
+}
+
+// The kk-th largest of the non-zero keys held one per lane (0 when fewer than kk lanes hold one):
+// the kk-th largest high word by a bit-by-bit search on ballots, then, among the lanes with that high
+// word, the low word that completes the count.  Keys are unique, so the result is one lane's key.
+__device__ __forceinline__ uint64_t wave_kth_largest(uint64_t key, int kk) {
+    const bool live = key != 0ull;
+    if (kk < 1 || __popcll(__ballot(live)) < kk) return 0ull;
+    const uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+    uint32_t vh = 0u;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = vh | (1u << b);
+        if (__popcll(__ballot(live && hi >= c)) >= kk) vh = c;
+    }
+    const int need = kk - __popcll(__ballot(live && hi > vh));   // >= 1
+    const bool eq = live && hi == vh;
+    const uint64_t eqm = __ballot(eq);
+    uint32_t vl;
+    if (__popcll(eqm) == 1) {
+        vl = (uint32_t)__builtin_amdgcn_readlane((int)lo, __builtin_ctzll(eqm));
+    } else {
+        vl = 0u;
+        for (int b = 31; b >= 0; --b) {
+            const uint32_t c = vl | (1u << b);
+            if (__popcll(__ballot(eq && lo >= c)) >= need) vl = c;
+        }
+    }
+    return ((uint64_t)vh << 32) | vl;
+}
+
+// Inclusive sum over the 64 lanes of the wave: row shifts, then row broadcasts.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);    // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);    // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);    // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);    // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Ascending ranks of ids below 2048 held by the lanes of one wave (a lane may hold two: a, b),
+// among all ids the wave holds: a 64-word LDS bitmap (word w = ids 32w .. 32w + 31), its prefix
+// popcounts, and one lookup per id.  words: 128 LDS words of the calling wave.  Returns -1 for an
+// id not held.
+__device__ __forceinline__ int2 wave_id_ranks(uint32_t *words, int a, bool ha, int b, bool hb) {
+    const int lane = threadIdx.x & 63;
+    words[lane] = 0u;
+    wave_lds_sync();
+    if (ha) atomicOr(&words[a >> 5], 1u << (a & 31));
+    if (hb) atomicOr(&words[b >> 5], 1u << (b & 31));
+    wave_lds_sync();
+    const int c = __popc(words[lane]);
+    words[64 + lane] = wave_incl_sum(c) - c;
+    wave_lds_sync();
+    int2 r = make_int2(-1, -1);
+    if (ha) r.x = (int)words[64 + (a >> 5)] + __popc(words[a >> 5] & ((1u << (a & 31)) - 1u));
+    if (hb) r.y = (int)words[64 + (b >> 5)] + __popc(words[b >> 5] & ((1u << (b & 31)) - 1u));
+    return r;
+}
+
+// gscore: the row's n block scores; agn: Gamma_e, ke ids ascending (then -1); keybuf: LDS,
+// kKeyScratch entries; qlist: LDS, kq entries; sel: the row's k = kq + ke selection entries in
+// global memory, or nullptr.  Returns false, with nothing written to qlist or sel, when more than
+// kCandMax blocks pass the bound (workgroup-uniform); the caller then takes the LDS path.  The
+// caller synchronises the workgroup before reading qlist.
+template <int NT>
+__device__ __forceinline__ bool pick_query_regs(const float *gscore, int n, const int32_t *agn, int ke, int kq,
+                                                uint64_t *keybuf, int32_t *qlist, int32_t *sel, SelectShared<NT> &sh) {
+    static_assert(NT % 64 == 0 && NT <= 256, "per-wave bitmaps must fit in keybuf[64, 192)");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int kpt = n <= NT ? 1 : n <= 2 * NT ? 2 : n <= 4 * NT ? 4 : 8;
+    const int base = tid * kpt;
+    const int eid = lane < ke ? agn[lane] : -1;
+    float sv[kRegPickMax];
+#pragma unroll
+    for (int j = 0; j < kRegPickMax; ++j) sv[j] = gscore[min(base + min(j, kpt - 1), n - 1)];
+    uint64_t *tmax = keybuf;                                  // [<= 64] chunk maxima
+    uint32_t *words = (uint32_t *)(keybuf + 64) + wv * 64;    // [64] this wave's Gamma_e bitmap
+    int32_t *win = (int32_t *)(keybuf + 192);                 // [64] winner ids by rank (many survivors)
+    uint64_t *cbuf = keybuf + 256;                            // [kCandMax] survivors
+    if (tid == 0) sh.bcast[3] = 0;
+    // this thread's Gamma_e members (kpt divides 32: its blocks share one bitmap word)
+    const bool has_e = eid >= 0 && eid < n;
+    words[lane] = 0u;
+    wave_lds_sync();
+    if (has_e) atomicOr(&words[eid >> 5], 1u << (eid & 31));
+    wave_lds_sync();
+    const uint32_t mine = (words[base >> 5] >> (base & 31)) & ((1u << kpt) - 1u);
+    uint64_t key[kRegPickMax];
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int j = 0; j < kRegPickMax; ++j) {
+        const int i = base + j;
+        const bool c = j < kpt && i < n && !((mine >> j) & 1u);
+        key[j] = c ? composite_key(order_key(sv[j]), i) : 0ull;
+        best = key[j] > best ? key[j] : best;
+    }
+    int ct = 1;                            // threads per chunk (within a quad): at most 64 chunks
+    while (ct < 4 && n > 64 * kpt * ct) ct *= 2;
+    if (ct >= 2) best = dpp_max64(best, 0);
+    if (ct >= 4) best = dpp_max64(best, 1);
+    const int nch = (n + kpt * ct - 1) / (kpt * ct);
+    if ((tid & (ct - 1)) == 0 && tid / ct < nch) tmax[tid / ct] = best;
+    wg_barrier();
+    // T0: the kq-th best chunk maximum (1, keeping every candidate, when fewer than kq chunks hold one)
+    uint64_t T0 = wave_kth_largest(lane < nch ? tmax[lane] : 0ull, kq);
+    if (T0 == 0ull) T0 = 1ull;
+    uint32_t keep = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegPickMax; ++j) keep |= (key[j] != 0ull && key[j] >= T0) ? (1u << j) : 0u;
+    // survivor slots: ballots per key index, one LDS atomic per wave
+    uint64_t bal[kRegPickMax];
+    int wtot = 0;
+#pragma unroll
+    for (int j = 0; j < kRegPickMax; ++j) {
+        bal[j] = __ballot((keep >> j) & 1u);
+        wtot += __popcll(bal[j]);
+    }
+    int pos = 0;
+    if (wtot) {
+        int got = 0;
+        if (lane == 0) got = atomicAdd(&sh.bcast[3], wtot);
+        pos = __builtin_amdgcn_readfirstlane(__shfl(got, 0, 64));
+    }
+#pragma unroll
+    for (int j = 0; j < kRegPickMax; ++j) {
+        if ((keep >> j) & 1u) {
+            const int p = pos + lanes_below(bal[j]);
+            if (p < kCandMax) cbuf[p] = key[j];
+        }
+        pos += __popcll(bal[j]);
+    }
+    wg_barrier();
+    const int total = sh.bcast[3];
+    if (total > kCandMax) return false;
+    int qid = -1;                          // wave 0: this lane's winner id, or -1
+    if (total > 64) {
+        if (tid < 64) win[lane] = -1;
+        wg_barrier();
+        rank_mark<NT>(cbuf, total, kq, [&](int, uint64_t c, int rank) { win[rank] = (int)(0xFFFFFFFFu - (uint32_t)c); });
+        wg_barrier();
+        if (tid < 64 && lane < kq) qid = win[lane];
+    } else if (tid < 64) {
+        const uint64_t c = lane < total ? cbuf[lane] : 0ull;
+        uint64_t kth = total > kq ? wave_kth_largest(c, kq) : 1ull;
+        if (c != 0ull && c >= kth) qid = (int)(0xFFFFFFFFu - (uint32_t)c);
+    }
+    if (tid < 64) {
+        uint32_t *lw = (uint32_t *)(keybuf + 64);   // [128] words for the id ranks (wave 0's bitmaps are done)
+        const bool hq = qid >= 0;
+        const int nq = __popcll(__ballot(hq)), ne = __popcll(__ballot(has_e));
+        const int qr = wave_id_ranks(lw, qid, hq, 0, false).x;
+        if (hq) qlist[qr] = qid;
+        for (int p = nq + lane; p < kq; p += 64) qlist[p] = -1;
+        if (sel) {
+            const int k = kq + ke;
+            const int2 ur = wave_id_ranks(lw, qid, hq, eid, has_e);
+            if (hq) sel[ur.x] = qid;
+            if (has_e) sel[ur.y] = eid;
+            for (int p = nq + ne + lane; p < k; p += 64) sel[p] = -1;
+        }
+    }
+    return true;
+}
+
 // LDS layout of the selection phase for a row of n blocks.
 struct RowLds {
     uint64_t *keys;     // [kKeyScratch] top-k scratch

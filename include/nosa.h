@@ -262,7 +262,8 @@ int nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *k_sto
  * out as from the two calls:
  * selected and agn_state exactly, out up to float32 summation order.  When the selection would
  * score a row in several workgroups and rank Gamma_q in a kernel of its own (rows of more than
- * 64 KiB of pooled keys and fewer than 256 rows; bf16; kq, ke > 0; n_blocks <= 512), the ranking
+ * 64 KiB of pooled keys and fewer than 256 rows; bf16; kq, ke > 0; n_blocks <= 512, or
+ * n_blocks <= 2048 with kq and ke at most 64), the ranking
  * moves into the attention launch instead: the splits over Gamma_e start at once, and each split
  * over Gamma_q ranks the row's Gamma_q itself, so the ranking hides under attention.  When one
  * 256-thread workgroup would both score-and-select a row and attend it in a single split (256 rows

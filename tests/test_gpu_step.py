@@ -21,8 +21,20 @@ CASES = {
                      ke=12, seed=51),
     "fused_g8_ragged": dict(batch=3, n_q_heads=8, n_kv_heads=1, head_dim=128, n_blocks=301, kq=37, ke=29, seed=52),
     "fused_d64_g2": dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_blocks=500, kq=40, ke=24, seed=53),
-    "fallback_long_rows": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=700, kq=20, ke=20,
+    # rows of 513 to 2048 blocks with both subsets of at most 64 blocks: Gamma_q ranked from registers
+    "fused_regs_700": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=700, kq=20, ke=20,
+                           seed=62),
+    "fused_regs_2048_kq64": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=2048, kq=64, ke=64,
+                                 seed=72),
+    "fused_regs_1500_sink_window": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=1500,
+                                        n_blocks_max=1600, kq=23, ke=41, n_sink=2, n_window=7, seed=73),
+    "fused_regs_140_d64": dict(batch=2, n_q_heads=8, n_kv_heads=1, head_dim=64, n_blocks=140, kq=5, ke=3, seed=74),
+    "fused_regs_100_g8": dict(batch=2, n_q_heads=8, n_kv_heads=1, head_dim=128, n_blocks=100, kq=6, ke=9, seed=76),
+    # longer rows, or a subset above 64 blocks: the two calls
+    "fallback_long_rows": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=2100, kq=20, ke=20,
                                seed=62),
+    "fallback_kq_above_64": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=700, kq=65, ke=20,
+                                 seed=75),
     "fused_sink_window": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=200, kq=16, ke=48,
                               n_sink=1, n_window=16, seed=54),
     # fallback: fp32, an empty subset, short rows, many rows
@@ -95,6 +107,50 @@ def test_decode_step_matches_two_calls_and_oracle(name):
     assert torch.equal(sel_b, sel_c)
     assert torch.equal(out_b.view(torch.int16) if out_b.dtype == torch.bfloat16 else out_b,
                        out_c.view(torch.int16) if out_c.dtype == torch.bfloat16 else out_c)
+
+
+@pytest.mark.parametrize("kq", [32, 64])
+def test_decode_step_clustered_scores(kq):
+    """Block scores rising with the block id, from crafted pooled keys: the best blocks crowd into the
+    last chunks, so the chunk-maximum bound lets nearly every block of the kq best 16-block chunks
+    through (2048 blocks per row).  That is about 500 candidates for kq = 32, which the register
+    ranking keeps, and about 1000 for kq = 64, more than its candidate buffer holds, so the LDS
+    ranking takes over.  Both must give the oracle's selection exactly (the scores are distinct and
+    computed identically on both sides) and the two calls' results."""
+    w = small_workload("clustered_%d" % kq, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_blocks=2048,
+                       kq=kq, ke=32, seed=71)
+    x = generate(w)
+    B, Hkv, d, n = w.batch, w.n_kv_heads, w.head_dim, w.n_blocks
+    G = w.n_q_heads // Hkv
+    print("case clustered kq", kq, flush=True)
+    # every sub-block of block b pools to (b + 1) * sign(qs_0) * e_0, qs the row's summed query heads,
+    # so that the block score is (b + 1) * |qs_0|
+    qs0 = H.as_f64(x["q"]).reshape(B, Hkv, G, d)[..., 0].sum(axis=-1)
+    kp_host = np.zeros((B, Hkv, 2 * n, d), dtype=np.float32)
+    kp_host[..., 0] = (np.repeat(np.arange(1, n + 1, dtype=np.float32), 2)[None, None, :] *
+                       np.sign(qs0).astype(np.float32)[..., None])
+    shape = H.shape_of(w)
+    q, k, v, ev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
+    kp = H.dev(kp_host.reshape(B * Hkv, 2 * n, d))
+    ws = N.workspace(shape)
+    agn0 = torch.full((w.rows, w.ke), -7, dtype=torch.int32, device="cuda")
+    sel_a, agn_a, out_a = _two_calls(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    sel_b, agn_b, out_b = _step(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b) and torch.equal(agn_a, agn_b)
+    s_ref = O.block_scores(x["q"], kp_host, n, 2)
+    assert H.check_selection(H.host(sel_b), H.host(agn_b), s_ref, x["evict"], w.kq, w.ke) == 0
+    # the query-aware part is the kq highest block ids outside Gamma_e
+    sel_h, agn_h = H.host(sel_b).reshape(B, Hkv, -1), H.host(agn_b).reshape(B, Hkv, -1)
+    for b in range(B):
+        for g in range(Hkv):
+            rest = [i for i in range(n - 1, -1, -1) if i not in set(agn_h[b, g].tolist())][:kq]
+            assert sorted(set(sel_h[b, g].tolist()) - set(agn_h[b, g].tolist())) == sorted(rest)
+    ref = O.attention(x["q"], x["k"], x["v"], sel_h)
+    print("clustered kq", kq, H.check_attention(H.host(out_b), ref, w.dtype, "clustered (one call)"))
+    sel_c, _, out_c = _step(shape, q, kp, ev, 0, agn0, k, v, w.nbmax, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_b, sel_c) and torch.equal(out_b.view(torch.int16), out_c.view(torch.int16))
 
 
 MULTI = {
