@@ -671,9 +671,8 @@ bool row_step_fits(int n_blocks, int k) {
 // Empty partials (max = -inf) carry nothing and are passed over.  The partials are read kChunk
 // splits at a time, every load issued before any is used (one memory round trip per chunk rather
 // than two per split); each chunk is folded in against the largest max seen so far.
-template <typename T, int D, int G>
+template <typename T, int D, int G, int kChunk>
 __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
-    constexpr int kChunk = 8;
     const int row = blockIdx.x / G, h = blockIdx.x - row * G;
     const int b = row / a.Hkv, g = row - b * a.Hkv;
     const int dd = threadIdx.x;
@@ -717,6 +716,17 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
 
 static hipError_t mark(hipEvent_t ev, hipStream_t st) { return ev ? hipEventRecord(ev, st) : hipSuccess; }
 
+// The merge reads up to 16 partial slots per memory round trip: 8 at a time when a row has no more
+// (fewer loads), else 16 (one round trip for the fused step's 16 splits at bs4/128K).
+template <typename T, int D, int G>
+static hipError_t launch_combine(const DecodeArgs &a, int rows, hipStream_t st) {
+    if (a.St <= 8)
+        combine_kernel<T, D, G, 8><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
+    else
+        combine_kernel<T, D, G, 16><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int G>
 static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st, bool merge, const KernelMarks &m) {
     hipError_t e = mark(m.start, st);
@@ -728,8 +738,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, int rows, hipStream_t st,
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(m.stop, st);
     if (e != hipSuccess || a.direct || !merge) return e;
-    combine_kernel<T, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
-    return hipGetLastError();
+    return launch_combine<T, D, G>(a, rows, st);
 }
 
 template <typename T, int D>
@@ -758,8 +767,7 @@ static hipError_t launch_step_t(const DecodeArgs &a, const SelectArgs &s, int ro
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(m.stop, st);
     if (e != hipSuccess) return e;
-    combine_kernel<uint16_t, D, G><<<dim3((unsigned)(rows * G)), dim3(D), 0, st>>>(a);
-    return hipGetLastError();
+    return launch_combine<uint16_t, D, G>(a, rows, st);
 }
 
 template <int D>
