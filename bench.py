@@ -8,7 +8,7 @@ tokens/s = batch / step time.  The timed steps are fresh ones (n_blocks_prev = 0
 part ranks every visible block); ms_per_step_steady_state times the same step with n_blocks_prev =
 n_blocks, where it ranks the previous step's members under strict eviction.
 
-  python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config C2] [--also C3,F1]
+  python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config C2] [--also C3,F1,C5]
                   [--no-cpu-baseline] [--no-offload] [--no-transfer]
 
 Prints one JSON line.  `value` is the headline workload (bs16 / 16K context by default); the
@@ -758,7 +758,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="C2")
-    ap.add_argument("--also", default="C3,F1", help="comma list of extra resident workloads ('' for none)")
+    ap.add_argument("--also", default="C3,F1,C5", help="comma list of extra resident workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU timing and the check of the timed outputs)")
     ap.add_argument("--no-offload", action="store_true", help="skip the 128-step offload loops (C4)")

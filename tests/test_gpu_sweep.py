@@ -5,8 +5,9 @@ against the oracle and against nosa_select + nosa_sparse_decode:
   * the pick inside the attention launch (long rows, few rows);
   * the two calls (everything else).
 Shapes vary over GQA groups 1 to 8, d 64 and 128, ragged budgets, empty query-aware or
-query-agnostic subsets, and sink / window blocks. Each case runs a second step in which three
-blocks arrive under strict eviction."""
+query-agnostic subsets, and sink / window blocks; a second set covers rows of 513 to 2048 blocks
+with both subsets of at most 64 blocks (the pick ranked from registers). Each case runs a second
+step in which three blocks arrive under strict eviction."""
 
 import os
 
@@ -56,6 +57,31 @@ def _cases():
 CASES = _cases()
 
 
+def _long_cases():
+    # few rows of 513 to 2045 blocks with both subsets of at most 64 blocks: the query-aware pick
+    # runs from registers inside the attention launch (the second step adds 3 blocks, still <= 2048)
+    rng = np.random.default_rng(int(os.environ.get("NOSA_SWEEP_SEED", "20261203")) + 1)
+    out = []
+    for i in range(N_LONG):
+        G = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2]))
+        n = int(rng.integers(513, 2046))
+        ke = int(rng.integers(1, 65))
+        kq = int(rng.integers(1, 65))
+        ns = nw = 0
+        if ke >= 3 and rng.random() < 0.4:
+            ns = int(rng.integers(0, 2))
+            nw = int(rng.integers(0, (ke - ns) // 2 + 1))
+        out.append(dict(batch=int(rng.integers(1, 3)), n_q_heads=hkv * G, n_kv_heads=hkv,
+                        head_dim=int(rng.choice([64, 128])), n_blocks=n, n_blocks_max=n + 3, kq=kq, ke=ke,
+                        n_sink=ns, n_window=nw, seed=2000 + i))
+    return out
+
+
+N_LONG = int(os.environ.get("NOSA_SWEEP_LONG_CASES", "12"))
+LONG_CASES = _long_cases()
+
+
 def _run(shape, q, kp, ev, n_prev, agn_in, k, v, nbmax, ws, one_call):
     R = shape.batch * shape.n_kv_heads
     agn = agn_in.clone()
@@ -72,9 +98,17 @@ def _run(shape, q, kp, ev, n_prev, agn_in, k, v, nbmax, ws, one_call):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_decode_step_random_shapes(case):
-    c = CASES[case]
-    print("case", case, c)
-    w = small_workload("sweep%d" % case, **c)
+    _sweep_case(CASES[case], "sweep%d" % case)
+
+
+@pytest.mark.parametrize("case", range(N_LONG))
+def test_decode_step_random_long_rows(case):
+    _sweep_case(LONG_CASES[case], "long%d" % case)
+
+
+def _sweep_case(c, label):
+    print("case", label, c, flush=True)
+    w = small_workload(label, **c)
     x = generate(w)
     shape0 = H.shape_of(w)
     q, k, v, ev = H.dev(x["q"]), H.dev(x["k"]), H.dev(x["v"]), H.dev(x["evict"])
@@ -95,7 +129,7 @@ def test_decode_step_random_shapes(case):
         H.check_selection(H.host(sel_b), H.host(agn_b), s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref, n_sink=ns,
                           n_window=nw)
         ref = O.attention(x["q"], x["k"], x["v"], H.host(sel_b).reshape(w.batch, w.n_kv_heads, w.k))
-        H.check_attention(H.host(out_b), ref, w.dtype, "case %d step %d (one call)" % (case, step))
-        H.check_attention(H.host(out_a), ref, w.dtype, "case %d step %d (two calls)" % (case, step))
+        H.check_attention(H.host(out_b), ref, w.dtype, "%s step %d (one call)" % (label, step))
+        H.check_attention(H.host(out_a), ref, w.dtype, "%s step %d (two calls)" % (label, step))
         _, agn_ref, _ = O.select(s_ref, x["evict"], w.kq, w.ke, n_prev, agn_ref, ns, nw)
         agn0 = agn_b
