@@ -45,7 +45,7 @@ typedef float acc_t;
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 
-/* Bits of the accumulator type of this build (32 or 64). */
+/* Bits of the accumulator type the oracle was compiled with (32 or 64). */
 int oracle_acc_bits(void)
 {
     return ACC_BITS;
