@@ -139,7 +139,7 @@ constexpr size_t kFusedRowBytes = 64 * 1024;
 PartPlan select_plan(const nosa_shape *s) {
     const int R = rows_of(s), n = s->n_blocks;
     const int threads = R >= kTargetWorkgroups / 2 ? 256 : 1024;
-    const int part_threads = n > kLongRowBlocks ? 1024 : 256;
+    const int part_threads = n > kLongRowBlocks ? 512 : 256;
     int P;
     if (s->select_parts > 0) {
         P = s->select_parts;
@@ -147,12 +147,13 @@ PartPlan select_plan(const nosa_shape *s) {
         const size_t row_bytes = (size_t)n * spb_of(s) * s->head_dim * sizeof(float);
         if (threads == 256 || row_bytes <= kFusedRowBytes) {
             P = 1;
-        } else if (part_threads == 1024) {
-            // A 1024-thread workgroup fills a CU, so the parts and the row's Gamma_e workgroup
-            // together take one CU each: all of them start at once.  (Measured on MI355X at 2048
-            // blocks per row and 32 rows: 7 parts 47.5 us per step, 4 parts 49.5 us, and 8 parts,
-            // whose last workgroups wait for a free CU, 50.8 us.)
-            P = kCUs / R - 1;
+        } else if (part_threads == 512) {
+            // Long rows: 512-thread parts, two per CU, so that the parts and the row's Gamma_e
+            // workgroup fill the 512 workgroup slots at once.  (Measured on MI355X at 2048 blocks
+            // per row and 32 rows, one-call step: 15 parts of 512 threads 35.2 us per step, against
+            // 36.2 us for 7 parts of 1024 threads, one per CU; with 1024-thread parts, 8 parts,
+            // whose last workgroups waited for a free CU, had been slower than 7.)
+            P = kTargetWorkgroups / R - 1;
             const int cap = n / kMinBlocksPerPart > 0 ? n / kMinBlocksPerPart : 1;
             if (P > cap) P = cap;
         } else {

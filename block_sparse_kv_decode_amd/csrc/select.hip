@@ -28,7 +28,7 @@
 //   (radix select as the fallback).  Outputs are compacted in ascending block id.  The
 //   selection's workgroup barriers wait for LDS only.
 // Launch plans (chosen on the host).  "fused": one workgroup (256 or 1024 threads) scores a
-//   whole row and selects from LDS.  "parts": several workgroups (256 threads, or 1024 for rows
+//   whole row and selects from LDS.  "parts": several workgroups (256 threads, or 512 for rows
 //   over 1024 blocks) score slices of a row into the workspace while one more workgroup per row
 //   picks Gamma_e from the eviction scores; a second kernel (1024 threads per row) picks Gamma_q,
 //   unless the one-call decode step ranks it inside its attention launch.  No workgroup ever
@@ -141,10 +141,10 @@ static hipError_t launch_select_t(const SelectArgs &a, int rows, int fused_threa
         return hipGetLastError();
     }
     const unsigned grid = (unsigned)(rows * (a.parts + (a.scores_only ? 0 : 1)));
-    if (part_threads == 1024) {
-        const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<1024>(a.n_blocks);
-        if ((e = allow_lds(score_part_kernel<T, D, SPB, 1024>, dyn0)) != hipSuccess) return e;
-        score_part_kernel<T, D, SPB, 1024><<<dim3(grid), dim3(1024), dyn0, st>>>(a);
+    if (part_threads == 512) {
+        const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<512>(a.n_blocks);
+        if ((e = allow_lds(score_part_kernel<T, D, SPB, 512>, dyn0)) != hipSuccess) return e;
+        score_part_kernel<T, D, SPB, 512><<<dim3(grid), dim3(512), dyn0, st>>>(a);
     } else {
         const size_t dyn0 = a.scores_only ? 0 : row_lds_bytes<256>(a.n_blocks);
         if ((e = allow_lds(score_part_kernel<T, D, SPB, 256>, dyn0)) != hipSuccess) return e;
