@@ -342,8 +342,8 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
 
     A step appends the previous step's token (nosa_append_kv into the pinned host pool and the
     pooled keys; workloads with whole blocks arriving per step have them in the pool beforehand),
-    selects, and runs nosa_offload_decode (gather on a copy stream, overlapped with attention over
-    the cache hits).  Every pass starts from the same state (empty cache, prompt pooled keys): one
+    selects, and runs nosa_offload_decode (the gather of the misses and attention over the cache hits
+    in one launch).  Every pass starts from the same state (empty cache, prompt pooled keys): one
     pass records miss counts, selections and query-agnostic subsets (for hit rate, bytes per step,
     locality, and a check of the strict-eviction bounds), three timed passes run the overlapped path;
     with `full`, three more run the serial calls (cache_update on the compute stream, then
@@ -497,8 +497,8 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
             cfg, "+1 token/step, appended to the pinned host pool" if append else
             "+%d block(s) arriving per step" % w.blocks_per_step, w.kq, w.ke,
             " (agnostic part incl. %d sink + %d window blocks)" % (w.n_sink, w.n_window) if w.n_window else "", steps),
-        "path": "%snosa_select + nosa_offload_decode (gather on a copy stream, overlapped with attention over the "
-                "hits)" % ("nosa_append_kv + " if append else ""),
+        "path": "%snosa_select + nosa_offload_decode (the gather of the misses and attention over the hits in one "
+                "launch)" % ("nosa_append_kv + " if append else ""),
         "hit_rate_warm": 1.0 - statistics.mean(misses[warm]) / (R * k),
         "fetched_bytes_per_step_warm": statistics.mean(fetched[warm]),
         "cold_step_fetched_bytes": fetched[0],

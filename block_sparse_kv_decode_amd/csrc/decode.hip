@@ -32,6 +32,7 @@
 // while the missed blocks are still in transit, and the missed blocks in a second launch that
 // reads their slots straight from the miss list (entry stride 2, per-row count), and one combine
 // merges both.
+#include "gather_core.h"
 #include "nosa_device.h"
 #include "nosa_internal.h"
 #include "select_core.h"
@@ -398,6 +399,28 @@ template <int D, int G>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ SplitShared<D, G> sh;
     const int row = blockIdx.x / a.S, sp = blockIdx.x - row * a.S;
+    const int n_use = a.count ? min(a.k_sel, a.count[row]) : a.k_sel;
+    const int j0 = sp * a.nbs, j1 = min(n_use, j0 + a.nbs);
+    decode_mfma_split<D, G>(a, row, sp, a.table + (size_t)row * a.k_sel * a.tab_stride, a.tab_stride, j0, j1, sh);
+}
+
+// ---- offloaded KV: the gather and the attention over the cache hits in one launch ----------
+// Workgroups [0, n_gather) run the persistent gather of the missed blocks (gather_blocks); the rest
+// are decode_mfma_kernel's splits over the hit-only table.  The two roles share no data: the hits'
+// slots are not written by this step's gather.  One launch on one stream overlaps them with no
+// cross-stream event between map, gather and attention; the launch after it (the missed blocks)
+// is ordered behind both.  The gather's workgroups come first in dispatch order.
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void hit_gather_kernel(DecodeArgs a, GatherArgs g, int n_gather) {
+    extern __shared__ __align__(16) unsigned char dyn[];   // the gather's start[rows + 1]
+    __shared__ SplitShared<D, G> sh;
+    __shared__ int wsum[kGatherThreads / 64];
+    if ((int)blockIdx.x < n_gather) {
+        gather_blocks(g, blockIdx.x, n_gather, (int *)dyn, wsum);
+        return;
+    }
+    const int bid = blockIdx.x - n_gather;
+    const int row = bid / a.S, sp = bid - row * a.S;
     const int n_use = a.count ? min(a.k_sel, a.count[row]) : a.k_sel;
     const int j0 = sp * a.nbs, j1 = min(n_use, j0 + a.nbs);
     decode_mfma_split<D, G>(a, row, sp, a.table + (size_t)row * a.k_sel * a.tab_stride, a.tab_stride, j0, j1, sh);
@@ -829,6 +852,29 @@ hipError_t launch_row_step(int d, int G, int spb, const DecodeArgs &a, const Sel
                            hipStream_t st, const KernelMarks &m) {
     return d == 128 ? launch_row_step_d<128>(G, spb, a, s, rows, st, m)
                     : launch_row_step_d<64>(G, spb, a, s, rows, st, m);
+}
+
+template <int D, int G>
+static hipError_t launch_hit_gather_t(const DecodeArgs &a, const GatherArgs &g, int rows, hipStream_t st) {
+    static_assert(kGatherThreads == 256, "the gather role runs in the attention's 256-thread workgroups");
+    const size_t dyn = sizeof(int) * (size_t)(g.rows + 1);
+    hit_gather_kernel<D, G><<<dim3((unsigned)(kGatherWorkgroups + rows * a.S)), dim3(256), dyn, st>>>(
+        a, g, kGatherWorkgroups);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_hit_gather_d(int G, const DecodeArgs &a, const GatherArgs &g, int rows, hipStream_t st) {
+    switch (G) {
+        case 1: return launch_hit_gather_t<D, 1>(a, g, rows, st);
+        case 2: return launch_hit_gather_t<D, 2>(a, g, rows, st);
+        case 4: return launch_hit_gather_t<D, 4>(a, g, rows, st);
+        default: return launch_hit_gather_t<D, 8>(a, g, rows, st);
+    }
+}
+
+hipError_t launch_hit_gather(int d, int G, const DecodeArgs &a, const GatherArgs &g, int rows, hipStream_t st) {
+    return d == 128 ? launch_hit_gather_d<128>(G, a, g, rows, st) : launch_hit_gather_d<64>(G, a, g, rows, st);
 }
 
 // merge: run combine_kernel over the St partial slots after this launch (unless direct).

@@ -118,6 +118,9 @@ hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int row
                          hipStream_t st);
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t st);
+// bf16: the gather (kGatherWorkgroups workgroups) and decode_mfma_kernel's splits over a.table in one
+// launch; no merge.
+hipError_t launch_hit_gather(int d, int G, const DecodeArgs &a, const GatherArgs &g, int rows, hipStream_t st);
 hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st);
 hipError_t launch_decode(int dtype, int d, int G, const DecodeArgs &a, int rows, hipStream_t st, bool merge,
                          const KernelMarks &marks = KernelMarks());

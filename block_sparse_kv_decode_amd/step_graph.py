@@ -1,8 +1,9 @@
 """HIP-graph capture of one offloaded decode step (launch orchestration only; no compute here).
 
 A decode step of the offload loop is a short chain of library calls -- nosa_append_kv,
-nosa_select, nosa_offload_decode (which forks the block gather onto a copy stream and joins it
-back) -- whose kernels run for tens of microseconds each.  A serving loop that waits for every
+nosa_select, nosa_offload_decode (which, for bf16, gathers the missed blocks in the same launch as
+the attention over the hits, and for fp32 forks the gather onto a copy stream and joins it back)
+-- whose kernels run for tens of microseconds each.  A serving loop that waits for every
 step pays the host-side launch cost of the whole chain on each step; replaying a captured graph
 pays one launch.
 
