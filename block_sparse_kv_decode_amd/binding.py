@@ -232,7 +232,8 @@ def workspace(shape: NosaShape, device=None):
 
 def nosa_offload_decode(shape, q, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list,
                         host_k, host_v, cache_k, cache_v, softmax_scale, out, ws, compute=None, copy=None) -> None:
-    """copy=None runs everything on the compute stream; pass a second stream to overlap the gather."""
+    """copy=None runs everything on the compute stream (bf16: the gather of the misses and the attention
+    over the hits in one launch); a second stream runs the gather there instead."""
     cs = _stream(compute)
     cp = cs if copy is None else _stream(copy)
     _check(lib.nosa_offload_decode(ctypes.byref(shape), _p(q), _p(selected), _p(slot_of_block), _p(block_of_slot),

@@ -588,10 +588,11 @@ int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *s
     const WsLayout L = ws_layout(shape);
     int32_t *tab_hit = (int32_t *)((char *)ws + L.tab_hit);
     hipEvent_t copied = nullptr;
-    // bf16: the gather and the attention over the hits share one launch on the compute stream, so
-    // no cross-stream event separates them (measured on MI355X at bs16/16K with 4.4% misses per
-    // step: 0.259 against 0.283 ms per step with the gather on the copy stream)
-    const bool one_launch = shape->dtype == NOSA_BF16;
+    // bf16 without a distinct copy stream: the gather and the attention over the hits share one
+    // launch on the compute stream, so no cross-stream event separates them (measured on MI355X at
+    // bs16/16K with 4.4% misses per step: 0.259 against 0.283 ms per step with the gather on a copy
+    // stream)
+    const bool one_launch = shape->dtype == NOSA_BF16 && (copy == nullptr || copy == compute);
     GatherArgs g;
     rc = cache_step(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k, host_v,
                     cache_k, cache_v, tab_hit, compute, copy, &copied, one_launch ? &g : nullptr);

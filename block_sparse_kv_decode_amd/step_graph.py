@@ -1,9 +1,9 @@
 """HIP-graph capture of one offloaded decode step (launch orchestration only; no compute here).
 
 A decode step of the offload loop is a short chain of library calls -- nosa_append_kv,
-nosa_select, nosa_offload_decode (which, for bf16, gathers the missed blocks in the same launch as
-the attention over the hits, and for fp32 forks the gather onto a copy stream and joins it back)
--- whose kernels run for tens of microseconds each.  A serving loop that waits for every
+nosa_select, nosa_offload_decode (which, without a copy stream, gathers the missed blocks of a bf16
+step in the same launch as the attention over the hits, and with one forks the gather onto it and
+joins it back) -- whose kernels run for tens of microseconds each.  A serving loop that waits for every
 step pays the host-side launch cost of the whole chain on each step; replaying a captured graph
 pays one launch.
 
@@ -17,7 +17,7 @@ steps where a block arrives).
 
 from __future__ import annotations
 
-from typing import Dict, Tuple
+from typing import Dict, Optional, Tuple
 
 import torch
 
@@ -32,7 +32,7 @@ class OffloadStepGraphs:
     allocated by the caller and kept alive as long as this object.  ``q``, ``k_new``, ``v_new`` and
     ``positions`` are the static input buffers refilled before each replay."""
 
-    def __init__(self, shape0: N.NosaShape, state: dict, copy_stream: torch.cuda.Stream, scale: float):
+    def __init__(self, shape0: N.NosaShape, state: dict, copy_stream: Optional[torch.cuda.Stream], scale: float):
         self.shape0 = shape0
         self.s = state
         self.copy = copy_stream

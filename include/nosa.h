@@ -319,13 +319,13 @@ int nosa_gather_units(const void *src, int64_t src_units, void *dst, int64_t dst
  * Offloaded decode step after selection: nosa_cache_update, then nosa_sparse_decode over the GPU
  * cache, with the host-to-GPU copy of the missed blocks overlapped with attention over the hit
  * blocks ([P1] §4: cached blocks are used in place and only missed blocks are moved; App. A: the
- * step is selection, transfer, attention).  bf16: everything runs on `compute`: the map kernel, then
- * one launch in which a few workgroups gather the misses while the others attend the hits (no
- * cross-stream event between them), then attention over the missed blocks and the merge of the two
- * parts with the online-softmax rule; `copy` is not used.  fp32: on `compute` the map kernel, then
- * attention over the hits; on `copy` (when it is a distinct stream) the gather of the misses;
- * `compute` then waits for the gather, attends the missed blocks and merges.  With copy NULL or
- * equal to compute everything runs on compute, in order.
+ * step is selection, transfer, attention).  With `copy` a distinct stream: on `compute` the map
+ * kernel, then attention over the hits; on `copy` the gather of the misses; `compute` then waits
+ * for the gather, attends the missed blocks and merges the two parts with the online-softmax rule.
+ * With copy NULL or equal to compute everything runs on compute, in order: for bf16 the map kernel,
+ * then one launch in which a few workgroups gather the misses while the others attend the hits (no
+ * cross-stream event between them, the faster form), then the missed blocks and the merge; for
+ * fp32 the map, the gather, the hits, the misses and the merge.
  * All arguments are those of nosa_cache_update and nosa_sparse_decode (store_blocks =
  * cache_slots, table = block_table).  slot_of_block, block_of_slot, block_table, miss_cnt,
  * miss_list and the cache contents come out exactly as from nosa_cache_update; `out` equals the
