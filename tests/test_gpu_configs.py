@@ -89,7 +89,9 @@ def test_decode_step_at_the_timed_shapes(cfg):
 def test_c4_offload_loop(cfg):
     """The 128-step offload loop: C4 (32 + 32, one token per step), C4P (the pages' 16 + 48 split with
     1 sink and a 16-block window), and the stress variants C4S / C4PS (one whole block arriving per
-    step, so that the query-agnostic subset drops its lowest member or the arrival every step)."""
+    step, so that the query-agnostic subset drops its lowest member or the arrival every step).
+    Even steps run nosa_offload_decode as the benchmark times it (no copy stream: the gather and the
+    attention over the hits in one launch), odd steps with the gather on a copy stream."""
     w = WORKLOADS[cfg]
     print("case", cfg, flush=True)
     x = generate(w)
@@ -150,7 +152,7 @@ def test_c4_offload_loop(cfg):
         sel, agn = H.gpu_select(shape, q_t, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
         out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
         N.nosa_offload_decode(shape, q_t, sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, scale, out, ws,
-                              copy=copy_stream)
+                              copy=copy_stream if t % 2 else None)
         torch.cuda.synchronize()
         sel_h = H.host(sel)
         mc = H.host(mcnt)

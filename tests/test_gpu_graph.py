@@ -1,6 +1,7 @@
-"""HIP-graph capture of the offloaded decode step (append, select, offload decode with the gather
-forked onto a copy stream): every replay is bit-identical to the same step run eagerly, with eager
-steps and synchronisations interleaved between replays, across the steps where blocks arrive."""
+"""HIP-graph capture of the offloaded decode step (append, select, offload decode, either with the
+gather and the attention over the hits in one launch or with the gather forked onto a copy stream):
+every replay is bit-identical to the same step run eagerly, with eager steps and synchronisations
+interleaved between replays, across the steps where blocks arrive."""
 
 import numpy as np
 import pytest
@@ -81,9 +82,11 @@ def _run(w, x, st, g, qs, steps, mode):
     return rec
 
 
-def test_offload_step_graph_replays_match_eager():
+@pytest.mark.parametrize("side_stream", [False, True])
+def test_offload_step_graph_replays_match_eager(side_stream):
     w, x, st, shape0, kfull, qs = _setup()
-    copy_stream = torch.cuda.Stream()
+    copy_stream = torch.cuda.Stream() if side_stream else None
+    print("case side_stream", side_stream, flush=True)
     g = OffloadStepGraphs(shape0, st, copy_stream, 1.0 / np.sqrt(w.head_dim))
     steps = 2 * BS + 3           # blocks arrive at steps 64 and 128
     _reset(w, st, shape0, kfull)
