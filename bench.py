@@ -348,8 +348,8 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
 
     A step appends the previous step's token (nosa_append_kv into the pinned host pool and the
     pooled keys; workloads with whole blocks arriving per step have them in the pool beforehand),
-    selects, and runs nosa_offload_decode (the gather of the misses and attention over the cache hits
-    in one launch).  Every pass starts from the same state (empty cache, prompt pooled keys): one
+    selects and runs the offloaded decode in one nosa_offload_step call (the cache map at the end of the
+    query-aware pick; the gather of the misses and attention over the cache hits in one launch).  Every pass starts from the same state (empty cache, prompt pooled keys): one
     pass records miss counts, selections and query-agnostic subsets (for hit rate, bytes per step,
     locality, and a check of the strict-eviction bounds), three timed passes run the overlapped path;
     with `full`, three more run the serial calls (cache_update on the compute stream, then
@@ -444,10 +444,17 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
                 evs[t][0].record(stream)
             if append and t > 0:
                 N.nosa_append_kv(shape0, new_k[t - 1], new_v[t - 1], positions[t], hkd, hvd, acc, kp, stream)
-            N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
+            if overlap == "step":
+                # nosa_select + nosa_offload_decode in one call (the cache map folded into the pick)
+                N.nosa_offload_step(shape, qs[t], kp, ev, n_prev, agn, sel, sob, bos, table, mcnt, mlist, hkd, hvd,
+                                    ck, cv, scale, out, ws, stream, None)
+            else:
+                N.nosa_select(shape, qs[t], kp, ev, n_prev, agn, sel, ws, stream)
             if phases:
                 evs[t][1].record(stream)
-            if overlap:
+            if overlap == "step":
+                pass
+            elif overlap:
                 # "side": the gather on a copy stream; otherwise gather and hit attention in one launch
                 N.nosa_offload_decode(shape, qs[t], sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, scale,
                                       out, ws, stream, copy_stream if overlap == "side" else None)
@@ -475,11 +482,11 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
             res["decode"] = [e[2].elapsed_time(e[3]) for e in evs]
         return res
 
-    loop(True, stats=True)                        # warm-up pass (code objects, host pool pages) + stats
+    loop("step", stats=True)                      # warm-up pass (code objects, host pool pages) + stats
     misses = mc_hist.sum(dim=1).cpu().numpy().tolist()
     s_h = sel_hist.cpu().numpy()
     a_h = agn_hist.cpu().numpy()
-    mean_ms = statistics.median([loop(True, timed=True)["warm_ms"] for _ in range(3)])
+    mean_ms = statistics.median([loop("step", timed=True)["warm_ms"] for _ in range(3)])
     # Locality and the strict-eviction bounds, every row and step: the query-agnostic subset changes
     # only by admitting arrivals (Gamma_e(t) within Gamma_e(t-1) and the arrivals A(t)), so adjacent
     # selections share at least ke - a(t) blocks, a(t) = admitted arrivals; gamma >= (ke - a(t)) / k.
@@ -504,8 +511,9 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
             cfg, "+1 token/step, appended to the pinned host pool" if append else
             "+%d block(s) arriving per step" % w.blocks_per_step, w.kq, w.ke,
             " (agnostic part incl. %d sink + %d window blocks)" % (w.n_sink, w.n_window) if w.n_window else "", steps),
-        "path": "%snosa_select + nosa_offload_decode (the gather of the misses and attention over the hits in one "
-                "launch)" % ("nosa_append_kv + " if append else ""),
+        "path": "%snosa_offload_step (the selection, the cache map folded into the query-aware pick, the gather of "
+                "the misses and attention over the hits in one launch, the misses, the merge)" % (
+                    "nosa_append_kv + " if append else ""),
         "hit_rate_warm": 1.0 - statistics.mean(misses[warm]) / (R * k),
         "fetched_bytes_per_step_warm": statistics.mean(fetched[warm]),
         "cold_step_fetched_bytes": fetched[0],
@@ -520,6 +528,7 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
         return res
     serial_ms = statistics.median([loop(False, timed=True)["warm_ms"] for _ in range(3)])
     side_ms = statistics.median([loop("side", timed=True)["warm_ms"] for _ in range(3)])
+    two_call_ms = statistics.median([loop(True, timed=True)["warm_ms"] for _ in range(3)])
     ph = loop(False, phases=True)
     # A serving loop waits for every step.  Host wall time per step with a synchronisation after
     # each, the step's calls launched eagerly vs replayed from captured HIP graphs (inputs copied
@@ -558,6 +567,7 @@ def run_offload(cfg="C4", full=True, steps_cap=None):
     res.update({
         "serial_step_ms_mean_warm": serial_ms,
         "side_stream_step_ms_mean_warm": side_ms,
+        "select_then_offload_decode_ms_mean_warm": two_call_ms,
         "serial_phase_ms_mean_warm": {"append_select": statistics.mean(ph["select"][warm]),
                                       "cache_update": cache_ms, "sparse_decode": statistics.mean(ph["decode"][warm])},
         "h2d_gbps_warm_serial_cache_update": statistics.mean(fetched[warm]) / (cache_ms * 1e-3) / 1e9,

@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     NOSA_OK, NosaError, NosaShape, lib, make_shape, nosa_block_scores, nosa_cache_update,
     nosa_last_error, nosa_pool_keys, nosa_append_kv, nosa_select, nosa_sparse_decode, nosa_version,
     nosa_offload_decode, nosa_gather_units, nosa_decode_step, nosa_host_map, host_map, nosa_profile_next_kernel,
-    nosa_profile_last_kernel, nosa_decode_step_noalloc,
+    nosa_profile_last_kernel, nosa_decode_step_noalloc, nosa_offload_step,
     nosa_workspace_bytes, workspace,
 )

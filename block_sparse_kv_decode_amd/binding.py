@@ -34,7 +34,7 @@ EXPORTED = (
     "nosa_last_error", "nosa_version", "nosa_workspace_bytes", "nosa_pool_keys", "nosa_append_kv",
     "nosa_block_scores", "nosa_select", "nosa_cache_update", "nosa_sparse_decode", "nosa_offload_decode",
     "nosa_gather_units", "nosa_decode_step", "nosa_host_map", "nosa_profile_next_kernel",
-    "nosa_profile_last_kernel", "nosa_decode_step_noalloc",
+    "nosa_profile_last_kernel", "nosa_decode_step_noalloc", "nosa_offload_step",
 )
 
 
@@ -103,6 +103,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_gather_units.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int64, P]
     L.nosa_offload_decode.restype = ctypes.c_int
     L.nosa_offload_decode.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
+    L.nosa_offload_step.restype = ctypes.c_int
+    L.nosa_offload_step.argtypes = [SP, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
     L.nosa_sparse_decode.restype = ctypes.c_int
     L.nosa_sparse_decode.argtypes = [SP, P, P, P, I32, P, ctypes.c_float, P, P, P]
     L.nosa_host_map.restype = ctypes.c_int
@@ -245,6 +247,18 @@ def nosa_gather_units(src, src_units, dst, dst_units, unit_bytes, src_unit, dst_
                       stream=None) -> None:
     _check(lib.nosa_gather_units(_dp(src), int(src_units), _dp(dst), int(dst_units), int(unit_bytes), _p(src_unit),
                                  _p(dst_unit), int(n_units), _stream(stream)))
+
+
+def nosa_offload_step(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, slot_of_block, block_of_slot,
+                      block_table, miss_cnt, miss_list, host_k, host_v, cache_k, cache_v, softmax_scale, out, ws,
+                      compute=None, copy=None) -> None:
+    """nosa_select then nosa_offload_decode in one call (streams as for nosa_offload_decode)."""
+    cs = _stream(compute)
+    cp = cs if copy is None else _stream(copy)
+    _check(lib.nosa_offload_step(ctypes.byref(shape), _p(q), _p(pooled_k), _p(evict), int(n_blocks_prev),
+                                 _p(agn_state), _p(selected), _p(slot_of_block), _p(block_of_slot), _p(block_table),
+                                 _p(miss_cnt), _p(miss_list), _dp(host_k), _dp(host_v), _p(cache_k), _p(cache_v),
+                                 ctypes.c_float(softmax_scale), _p(out), _p(ws), cs, cp))
 
 
 def nosa_decode_step(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, k_store, v_store, store_blocks,

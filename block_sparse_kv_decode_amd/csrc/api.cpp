@@ -451,11 +451,11 @@ int nosa_select(const nosa_shape *shape, const void *q, const float *pooled_k, c
 // Validation and launches shared by nosa_cache_update and nosa_offload_decode.  With a distinct
 // copy stream the gather runs there, after the map (event), and *copied is set to an event that
 // marks its end; the caller makes the compute stream wait on it.
-static int cache_step(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
+// Validation of the cache step's arguments, and the map's and the gather's kernel arguments.
+static int cache_plan(const nosa_shape *shape, const int32_t *selected, int32_t *slot_of_block,
                       int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
                       const void *host_k, const void *host_v, void *cache_k, void *cache_v, int32_t *table_hit,
-                      hipStream_t compute, hipStream_t copy, hipEvent_t *copied, GatherArgs *defer = nullptr) {
-    *copied = nullptr;
+                      CacheArgs *c, GatherArgs *g) {
     const int k = shape->kq + shape->ke;
     if (shape->cache_slots < k)
         return fail(NOSA_ECAPACITY, "cache_slots %d is below the budget kq + ke = %d", shape->cache_slots, k);
@@ -474,39 +474,44 @@ static int cache_step(const nosa_shape *shape, const int32_t *selected, int32_t 
     REQUIRE_PTR(host_v, 16);
     REQUIRE_PTR(cache_k, 16);
     REQUIRE_PTR(cache_v, 16);
+    c->sel = selected;
+    c->sob = slot_of_block;
+    c->bos = block_of_slot;
+    c->table = block_table;
+    c->mcnt = miss_cnt;
+    c->mlist = miss_list;
+    c->table_hit = table_hit;
+    c->k = k;
+    c->C = shape->cache_slots;
+    c->nbmax = shape->n_blocks_max;
+    g->hk = (const unsigned char *)host_k;
+    g->hv = (const unsigned char *)host_v;
+    g->ck = (unsigned char *)cache_k;
+    g->cv = (unsigned char *)cache_v;
+    g->mcnt = miss_cnt;
+    g->mlist = miss_list;
+    g->rows = rows_of(shape);
+    g->k = k;
+    g->C = shape->cache_slots;
+    g->nbmax = shape->n_blocks_max;
+    g->block_bytes = (long long)shape->block_size * shape->head_dim * (long long)elem_bytes(shape);
+    return NOSA_OK;
+}
 
-    const int R = rows_of(shape);
-    CacheArgs c;
-    c.sel = selected;
-    c.sob = slot_of_block;
-    c.bos = block_of_slot;
-    c.table = block_table;
-    c.mcnt = miss_cnt;
-    c.mlist = miss_list;
-    c.table_hit = table_hit;
-    c.k = k;
-    c.C = shape->cache_slots;
-    c.nbmax = shape->n_blocks_max;
-    hipError_t e = launch_cache_map(c, R, compute);
-    if (e != hipSuccess) return hip_fail(e, "cache_map launch");
-
-    GatherArgs g;
-    g.hk = (const unsigned char *)host_k;
-    g.hv = (const unsigned char *)host_v;
-    g.ck = (unsigned char *)cache_k;
-    g.cv = (unsigned char *)cache_v;
-    g.mcnt = miss_cnt;
-    g.mlist = miss_list;
-    g.rows = R;
-    g.k = k;
-    g.C = shape->cache_slots;
-    g.nbmax = shape->n_blocks_max;
-    g.block_bytes = (long long)shape->block_size * shape->head_dim * (long long)elem_bytes(shape);
+// The launches shared by nosa_cache_update, nosa_offload_decode and nosa_offload_step: the map
+// (unless map_done: the caller has run it), then the gather.  With a distinct copy stream the
+// gather runs there, after the map (event), and *copied is set to an event that marks its end; the
+// caller makes the compute stream wait on it.  With defer the caller launches the gather itself.
+static int cache_step(const nosa_shape *shape, const CacheArgs &c, const GatherArgs &g, bool map_done,
+                      hipStream_t compute, hipStream_t copy, hipEvent_t *copied, GatherArgs *defer = nullptr) {
+    *copied = nullptr;
+    hipError_t e;
+    if (!map_done && (e = launch_cache_map(c, rows_of(shape), compute)) != hipSuccess)
+        return hip_fail(e, "cache_map launch");
     if (defer) {   // the caller launches the gather
         *defer = g;
         return NOSA_OK;
     }
-
     if (copy == nullptr || copy == compute) {
         e = launch_gather(g, compute);
         return e == hipSuccess ? NOSA_OK : hip_fail(e, "gather launch");
@@ -567,15 +572,52 @@ int nosa_cache_update(const nosa_shape *shape, const int32_t *selected, int32_t 
                       hipStream_t copy) {
     int rc = check_shape(shape);
     if (rc) return rc;
+    CacheArgs c;
+    GatherArgs g;
+    if ((rc = cache_plan(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k,
+                         host_v, cache_k, cache_v, nullptr, &c, &g)) != NOSA_OK)
+        return rc;
     hipEvent_t copied = nullptr;
-    rc = cache_step(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k, host_v,
-                    cache_k, cache_v, nullptr, compute, copy, &copied);
-    if (rc) return rc;
+    if ((rc = cache_step(shape, c, g, false, compute, copy, &copied)) != NOSA_OK) return rc;
     if (copied) {
         hipError_t e = hipStreamWaitEvent(compute, copied, 0);
         if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     }
     return ok();
+}
+
+// The offloaded decode after the selection: the map (unless map_done), the gather and the attention
+// over the hits, then the misses and one merge.  Arguments validated by the caller.
+static int offload_decode_run(const nosa_shape *shape, const void *q, const CacheArgs &c, const GatherArgs &g,
+                              bool map_done, const int32_t *miss_list, const int32_t *miss_cnt, void *cache_k,
+                              void *cache_v, const int32_t *tab_hit, float softmax_scale, void *out, void *ws,
+                              hipStream_t compute, hipStream_t copy) {
+    hipEvent_t copied = nullptr;
+    // bf16 without a distinct copy stream: the gather and the attention over the hits share one
+    // launch on the compute stream, so no cross-stream event separates them (measured on MI355X at
+    // bs16/16K with 4.4% misses per step: 0.259 against 0.283 ms per step with the gather on a copy
+    // stream)
+    const bool one_launch = shape->dtype == NOSA_BF16 && (copy == nullptr || copy == compute);
+    GatherArgs gd;
+    int rc = cache_step(shape, c, g, map_done, compute, copy, &copied, one_launch ? &gd : nullptr);
+    if (rc) return rc;
+    // hits: attended while the misses are in transit (partial slots [0, S))
+    DecodeArgs a = decode_args(shape, q, cache_k, cache_v, shape->cache_slots, softmax_scale, out, ws);
+    a.table = tab_hit;
+    a.St = 2 * a.S;
+    a.direct = 0;
+    const int G = group_of(shape), R = rows_of(shape);
+    hipError_t e = one_launch ? launch_hit_gather(shape->head_dim, G, a, gd, R, compute)
+                              : launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, false);
+    if (e != hipSuccess) return hip_fail(e, "offload_decode hit launch");
+    if (copied && (e = hipStreamWaitEvent(compute, copied, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    // misses: their cache slots straight from the miss list (slots [S, 2S)), then one merge
+    a.table = miss_list + 1;
+    a.tab_stride = 2;
+    a.count = miss_cnt;
+    a.s0 = a.S;
+    e = launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, true);
+    return e == hipSuccess ? ok() : hip_fail(e, "offload_decode miss launch");
 }
 
 int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *selected, int32_t *slot_of_block,
@@ -587,33 +629,50 @@ int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *s
     if ((rc = check_decode_args(q, cache_k, cache_v, shape->cache_slots, softmax_scale, out, ws)) != NOSA_OK) return rc;
     const WsLayout L = ws_layout(shape);
     int32_t *tab_hit = (int32_t *)((char *)ws + L.tab_hit);
-    hipEvent_t copied = nullptr;
-    // bf16 without a distinct copy stream: the gather and the attention over the hits share one
-    // launch on the compute stream, so no cross-stream event separates them (measured on MI355X at
-    // bs16/16K with 4.4% misses per step: 0.259 against 0.283 ms per step with the gather on a copy
-    // stream)
-    const bool one_launch = shape->dtype == NOSA_BF16 && (copy == nullptr || copy == compute);
+    CacheArgs c;
     GatherArgs g;
-    rc = cache_step(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k, host_v,
-                    cache_k, cache_v, tab_hit, compute, copy, &copied, one_launch ? &g : nullptr);
+    if ((rc = cache_plan(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k,
+                         host_v, cache_k, cache_v, tab_hit, &c, &g)) != NOSA_OK)
+        return rc;
+    return offload_decode_run(shape, q, c, g, false, miss_list, miss_cnt, cache_k, cache_v, tab_hit, softmax_scale,
+                              out, ws, compute, copy);
+}
+
+int nosa_offload_step(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                      int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, int32_t *slot_of_block,
+                      int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
+                      const void *host_k, const void *host_v, void *cache_k, void *cache_v, float softmax_scale,
+                      void *out, void *ws, hipStream_t compute, hipStream_t copy) {
+    int rc = check_shape(shape);
     if (rc) return rc;
-    // hits: attended while the misses are in transit (partial slots [0, S))
-    DecodeArgs a = decode_args(shape, q, cache_k, cache_v, shape->cache_slots, softmax_scale, out, ws);
-    a.table = tab_hit;
-    a.St = 2 * a.S;
-    a.direct = 0;
-    const int G = group_of(shape), R = rows_of(shape);
-    hipError_t e = one_launch ? launch_hit_gather(shape->head_dim, G, a, g, R, compute)
-                              : launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, false);
-    if (e != hipSuccess) return hip_fail(e, "offload_decode hit launch");
-    if (copied && (e = hipStreamWaitEvent(compute, copied, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    // misses: their cache slots straight from the miss list (slots [S, 2S)), then one merge
-    a.table = miss_list + 1;
-    a.tab_stride = 2;
-    a.count = miss_cnt;
-    a.s0 = a.S;
-    e = launch_decode(shape->dtype, shape->head_dim, G, a, R, compute, true);
-    return e == hipSuccess ? ok() : hip_fail(e, "offload_decode miss launch");
+    if ((rc = check_decode_args(q, cache_k, cache_v, shape->cache_slots, softmax_scale, out, ws)) != NOSA_OK) return rc;
+    const WsLayout L = ws_layout(shape);
+    int32_t *tab_hit = (int32_t *)((char *)ws + L.tab_hit);
+    CacheArgs c;
+    GatherArgs g;
+    if ((rc = cache_plan(shape, selected, slot_of_block, block_of_slot, block_table, miss_cnt, miss_list, host_k,
+                         host_v, cache_k, cache_v, tab_hit, &c, &g)) != NOSA_OK)
+        return rc;
+    SelectArgs sa;
+    // validation of the selection's arguments, before anything is launched
+    if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, compute, false,
+                         &sa, true)) != NOSA_OK)
+        return rc;
+    // Rows scored in parts take their Gamma_q pick in a kernel of its own: the rows' cache maps
+    // run at its end instead of in a launch of their own.
+    const bool fold_map = select_plan(shape).P > 1;
+    if (fold_map) {
+        if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws, compute,
+                             true, &sa)) != NOSA_OK)
+            return rc;
+        hipError_t e = launch_pick_map(sa, c, rows_of(shape), compute);
+        if (e != hipSuccess) return hip_fail(e, "pick_map launch");
+    } else if ((rc = run_scores(shape, q, pooled_k, evict, n_blocks_prev, agn_state, selected, nullptr, ws,
+                                compute)) != NOSA_OK) {
+        return rc;
+    }
+    return offload_decode_run(shape, q, c, g, fold_map, miss_list, miss_cnt, cache_k, cache_v, tab_hit,
+                              softmax_scale, out, ws, compute, copy);
 }
 
 int nosa_decode_step(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,

@@ -14,77 +14,17 @@
 // gather: a small persistent grid walks the flattened miss list; for each miss a workgroup copies
 //   one K block and one V block from the device-mapped pinned host pool into the cache slot with
 //   16-byte loads.
+#include "cache_core.h"
 #include "gather_core.h"
 #include "nosa_device.h"
 #include "nosa_internal.h"
 
 namespace nosa {
 
+// One wave per row (cache_map_row in cache_core.h).
 __global__ __launch_bounds__(64) void cache_map_kernel(CacheArgs a) {
     extern __shared__ __align__(16) unsigned char dyn[];
-    const int k = a.k, C = a.C;
-    const int cpad = (C + 15) & ~15;
-    uint8_t *held = dyn;                        // [C] slot holds a hit
-    int *miss_blk = (int *)(dyn + cpad);        // [k]
-    int *miss_pos = miss_blk + k;               // [k]
-    int *free_slot = miss_pos + k;              // [k]
-
-    const int row = blockIdx.x, lane = threadIdx.x;
-    const int32_t *sel = a.sel + (size_t)row * k;
-    int32_t *sob = a.sob + (size_t)row * a.nbmax;
-    int32_t *bos = a.bos + (size_t)row * C;
-    int32_t *table = a.table + (size_t)row * k;
-
-    for (int s = lane; s < C; s += 64) held[s] = 0;
-    __syncthreads();
-
-    int nmiss = 0;
-    for (int base = 0; base < k; base += 64) {
-        const int i = base + lane;
-        const bool valid = i < k;
-        const int blk = valid ? sel[i] : -1;
-        const bool inr = valid && (unsigned)blk < (unsigned)a.nbmax;
-        const int slot = inr ? sob[blk] : -1;
-        const bool hit = inr && slot >= 0 && slot < C;
-        if (hit) held[slot] = 1;
-        if (valid) table[i] = hit ? slot : -1;
-        if (valid && a.table_hit) a.table_hit[(size_t)row * k + i] = hit ? slot : -1;
-        const bool miss = inr && !hit;
-        const uint64_t mm = __ballot(miss);
-        if (miss) {
-            const int r = nmiss + lanes_below(mm);
-            miss_blk[r] = blk;
-            miss_pos[r] = i;
-        }
-        nmiss += __popcll(mm);
-    }
-    __syncthreads();
-
-    int nfree = 0;
-    for (int base = 0; base < C && nfree < nmiss; base += 64) {
-        const int s = base + lane;
-        const bool f = s < C && !held[s];
-        const uint64_t fm = __ballot(f);
-        if (f) {
-            const int r = nfree + lanes_below(fm);
-            if (r < nmiss) free_slot[r] = s;
-        }
-        nfree += __popcll(fm);
-    }
-    __syncthreads();
-
-    const int nuse = min(nmiss, nfree);
-    for (int r = lane; r < nuse; r += 64) {
-        const int s = free_slot[r], blk = miss_blk[r];
-        const int old = bos[s];
-        if ((unsigned)old < (unsigned)a.nbmax) sob[old] = -1;
-        sob[blk] = s;
-        bos[s] = blk;
-        table[miss_pos[r]] = s;
-        a.mlist[((size_t)row * k + r) * 2 + 0] = blk;
-        a.mlist[((size_t)row * k + r) * 2 + 1] = s;
-    }
-    if (lane == 0) a.mcnt[row] = nuse;
+    cache_map_row(a, blockIdx.x, threadIdx.x, dyn);
 }
 
 // Persistent gather (gather_blocks in gather_core.h), on its own.
@@ -138,7 +78,7 @@ hipError_t launch_gather_units(const UnitsArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st) {
-    const size_t dyn = (size_t)((a.C + 15) & ~15) + 3 * sizeof(int) * (size_t)a.k;
+    const size_t dyn = cache_map_lds_bytes(a.C, a.k);
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)cache_map_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;

@@ -114,6 +114,8 @@ hipError_t launch_pool(int dtype, int d, const PoolArgs &a, int rows, hipStream_
 hipError_t launch_append(int dtype, int d, const AppendArgs &a, int rows, hipStream_t st);
 // fused_threads: workgroup size (256 or 1024) of the one-workgroup-per-row plan (parts == 1);
 // part_threads: workgroup size (256 or 1024) of the multi-part scoring kernel.
+// The Gamma_q pick of rows scored in parts (pick_kernel), then each row's cache map (one wave).
+hipError_t launch_pick_map(const SelectArgs &a, const CacheArgs &c, int rows, hipStream_t st);
 hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads, int part_threads,
                          hipStream_t st);
 hipError_t launch_cache_map(const CacheArgs &a, int rows, hipStream_t st);

@@ -33,6 +33,7 @@
 //   picks Gamma_e from the eviction scores; a second kernel (1024 threads per row) picks Gamma_q,
 //   unless the one-call decode step ranks it inside its attention launch.  No workgroup ever
 //   waits on another inside a kernel.
+#include "cache_core.h"
 #include "select_core.h"
 
 namespace nosa {
@@ -115,6 +116,34 @@ __global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
     select_query<NT>(a, row, L, sh, false);
 }
 
+// pick_kernel, then the row's cache map (cache_map_row, by wave 0) from the selection just written:
+// the one-call offloaded step folds the map into the pick instead of launching it on its own.
+template <int NT>
+__global__ __launch_bounds__(NT) void pick_map_kernel(SelectArgs a, CacheArgs c) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ SelectShared<NT> sh;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    {
+        const RowLds L = carve<NT>(dyn, a.n_blocks);
+        const float *gscore = a.scores + (size_t)row * a.scores_stride;
+        const int32_t *agn = a.agn + (size_t)row * a.ke;
+        const int id0 = tid < a.ke ? agn[tid] : -1;
+        scores_to_lds<NT>(gscore, a.n_blocks, L);
+        __syncthreads();
+        if (id0 >= 0 && id0 < a.n_blocks) L.inE[id0] = 1;
+        for (int j = tid + NT; j < a.ke; j += NT) {
+            const int id = agn[j];
+            if (id >= 0 && id < a.n_blocks) L.inE[id] = 1;
+        }
+        __syncthreads();
+        select_query<NT>(a, row, L, sh, false);
+    }
+    // the row's selection (global stores of every wave) is visible to the workgroup after the
+    // barrier; the pick's LDS is free again
+    __syncthreads();
+    if (tid < 64) cache_map_row(c, row, tid, dyn);
+}
+
 
 template <class K>
 static hipError_t allow_lds(K kern, size_t dyn) {
@@ -168,6 +197,15 @@ static hipError_t launch_select_d(int spb, const SelectArgs &a, int rows, int fu
         case 4: return launch_select_t<T, D, 4>(a, rows, fused_threads, part_threads, st);
         default: return launch_select_t<T, D, 8>(a, rows, fused_threads, part_threads, st);
     }
+}
+
+hipError_t launch_pick_map(const SelectArgs &a, const CacheArgs &c, int rows, hipStream_t st) {
+    size_t dyn = row_lds_bytes<1024>(a.n_blocks);
+    if (cache_map_lds_bytes(c.C, c.k) > dyn) dyn = cache_map_lds_bytes(c.C, c.k);
+    hipError_t e = allow_lds(pick_map_kernel<1024>, dyn);
+    if (e != hipSuccess) return e;
+    pick_map_kernel<1024><<<dim3((unsigned)rows), dim3(1024), dyn, st>>>(a, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_select(int dtype, int d, int spb, const SelectArgs &a, int rows, int fused_threads,

@@ -339,6 +339,24 @@ int nosa_offload_decode(const nosa_shape *shape, const void *q, const int32_t *s
                         void *cache_k, void *cache_v, float softmax_scale, void *out, void *ws,
                         hipStream_t compute, hipStream_t copy);
 
+/*
+ * One offloaded decode step in one call: nosa_select, then nosa_offload_decode ([P1] App. A: per
+ * step, selection, transfer of the missed blocks, attention; §4: the replacement map from the set
+ * difference of the selections).  Arguments: those of nosa_select (q, pooled_k, evict,
+ * n_blocks_prev, agn_state, selected) and of nosa_offload_decode (the rest), with the same layouts
+ * and ownership; ws from nosa_workspace_bytes of a shape with cache_slots >= kq + ke.  Outputs
+ * equal those of the two calls made in order: agn_state, selected, the slot maps, block table,
+ * miss list and cache contents bit for bit, `out` up to float32 summation order.  When the rows are
+ * scored in parts (the selection's Gamma_q pick is a kernel of its own), each row's cache map runs
+ * at the end of its pick instead of in a launch of its own.  Streams as for nosa_offload_decode.
+ * Every argument is validated on the host before any launch; errors as for the two calls.
+ */
+int nosa_offload_step(const nosa_shape *shape, const void *q, const float *pooled_k, const float *evict,
+                      int32_t n_blocks_prev, int32_t *agn_state, int32_t *selected, int32_t *slot_of_block,
+                      int32_t *block_of_slot, int32_t *block_table, int32_t *miss_cnt, int32_t *miss_list,
+                      const void *host_k, const void *host_v, void *cache_k, void *cache_v, float softmax_scale,
+                      void *out, void *ws, hipStream_t compute, hipStream_t copy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,6 +161,23 @@ def test_offload_decode_rejects_on_host():
     with pytest.raises(N.NosaError) as ei:      # bad scale
         N.nosa_offload_decode(s, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, 256, compute=0, copy=0)
     assert ei.value.code == N.NOSA_EINVAL
+    # the one-call offloaded step validates the cache, decode and selection arguments before any launch
+    with pytest.raises(N.NosaError) as ei:      # cache below the budget
+        N.nosa_offload_step(_good(cache_slots=10), 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 0.1, 16,
+                            256, compute=0, copy=0)
+    assert ei.value.code == N.NOSA_ECAPACITY
+    with pytest.raises(N.NosaError) as ei:      # miss_list NULL
+        N.nosa_offload_step(s, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, 16, 0.1, 16, 256, compute=0,
+                            copy=0)
+    assert ei.value.code == N.NOSA_EINVAL
+    with pytest.raises(N.NosaError) as ei:      # pooled keys NULL
+        N.nosa_offload_step(s, 16, None, 16, 0, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 0.1, 16, 256, compute=0,
+                            copy=0)
+    assert ei.value.code == N.NOSA_EINVAL
+    with pytest.raises(N.NosaError) as ei:      # n_blocks_prev beyond n_blocks
+        N.nosa_offload_step(s, 16, 16, 16, s.n_blocks + 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 0.1, 16, 256,
+                            compute=0, copy=0)
+    assert ei.value.code == N.NOSA_EINVAL
     # the workspace grows by the hit table and the second set of partial slots when a cache is set
     assert N.nosa_workspace_bytes(_good(cache_slots=64)) > N.nosa_workspace_bytes(_good(cache_slots=0))
 

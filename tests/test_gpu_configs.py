@@ -90,8 +90,10 @@ def test_c4_offload_loop(cfg):
     """The 128-step offload loop: C4 (32 + 32, one token per step), C4P (the pages' 16 + 48 split with
     1 sink and a 16-block window), and the stress variants C4S / C4PS (one whole block arriving per
     step, so that the query-agnostic subset drops its lowest member or the arrival every step).
-    Even steps run nosa_offload_decode as the benchmark times it (no copy stream: the gather and the
-    attention over the hits in one launch), odd steps with the gather on a copy stream."""
+    Steps t = 0 mod 3 run nosa_offload_step as the benchmark times it (selection and offloaded decode in
+    one call, no copy stream); steps t = 1 mod 3 run nosa_select + nosa_offload_decode without a copy
+    stream (the gather and the attention over the hits in one launch), steps t = 2 mod 3 with the
+    gather on a copy stream."""
     w = WORKLOADS[cfg]
     print("case", cfg, flush=True)
     x = generate(w)
@@ -149,10 +151,17 @@ def test_c4_offload_loop(cfg):
             N.nosa_append_kv(shape0, kn_all[t - 1], vn_all[t - 1],
                              torch.full((w.batch,), pos, dtype=torch.int32, device="cuda"), hkd, hvd, acc, kp)
         q_t = q_all[t]
-        sel, agn = H.gpu_select(shape, q_t, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
         out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-        N.nosa_offload_decode(shape, q_t, sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, scale, out, ws,
-                              copy=copy_stream if t % 2 else None)
+        if t % 3 == 0:
+            if agn is None:
+                agn = torch.full((R, w.ke), -7, dtype=torch.int32, device="cuda")
+            sel = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+            N.nosa_offload_step(shape, q_t, kp, ev_dev, n_prev, agn, sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck,
+                                cv, scale, out, ws)
+        else:
+            sel, agn = H.gpu_select(shape, q_t, kp, ev_dev, ws, n_prev=n_prev, agn=agn)
+            N.nosa_offload_decode(shape, q_t, sel, sob, bos, table, mcnt, mlist, hkd, hvd, ck, cv, scale, out, ws,
+                                  copy=copy_stream if t % 3 == 2 else None)
         torch.cuda.synchronize()
         sel_h = H.host(sel)
         mc = H.host(mcnt)
