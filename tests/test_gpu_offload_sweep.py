@@ -1,5 +1,6 @@
-"""A seeded sweep of random shapes through the offloaded step, nosa_offload_decode: cache size,
-GQA group, head dim, dtype, budget split and the copy stream vary.  Over five steps with query drift
+"""A seeded sweep of random shapes through the offloaded step, nosa_select + nosa_offload_decode and
+nosa_offload_step on alternate steps: cache size, GQA group, head dim, dtype, budget split and the
+copy stream vary.  Over five steps with query drift
 and arriving blocks, the GPU's slot maps, block table, miss list and cache bytes must equal the
 oracle's cache simulation exactly, and attention over the cache must match the oracle's attention
 over the selected blocks."""
@@ -77,10 +78,19 @@ def test_offload_decode_random_shapes(case):
             n += 1 + t // 2
         shape = shape0.copy(n_blocks=n)
         q_dev = H.dev(qf)
-        sel, agn = H.gpu_select(shape, q_dev, kp, ev, ws, n_prev=n_prev, agn=agn)
         out = torch.full((w.batch, w.n_q_heads, d), float("nan"), dtype=tdt, device="cuda")
-        N.nosa_offload_decode(shape, q_dev, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out, ws,
-                              copy=copy_stream)
+        if (case + t) % 2 == 0:
+            # selection and offloaded decode in one call (the cache map inside the pick on rows scored
+            # in parts)
+            if agn is None:
+                agn = torch.full((R, max(w.ke, 1)), -7, dtype=torch.int32, device="cuda")
+            sel = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+            N.nosa_offload_step(shape, q_dev, kp, ev, n_prev, agn, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv,
+                                scale, out, ws, copy=copy_stream)
+        else:
+            sel, agn = H.gpu_select(shape, q_dev, kp, ev, ws, n_prev=n_prev, agn=agn)
+            N.nosa_offload_decode(shape, q_dev, sel, sob, bos, table, mcnt, mlist, hk, hv, ck, cv, scale, out, ws,
+                                  copy=copy_stream)
         torch.cuda.synchronize()
         sel_h = H.host(sel)
         tab_ref, mc_ref, ml_ref = O.cache_step(sel_h, sob_ref, bos_ref)
