@@ -30,8 +30,9 @@
 // Launch plans (chosen on the host).  "fused": one workgroup (256 or 1024 threads) scores a
 //   whole row and selects from LDS.  "parts": several workgroups (256 threads, or 512 for rows
 //   over 1024 blocks) score slices of a row into the workspace while one more workgroup per row
-//   picks Gamma_e from the eviction scores; a second kernel (1024 threads per row) picks Gamma_q,
-//   unless the one-call decode step ranks it inside its attention launch.  No workgroup ever
+//   picks Gamma_e from the eviction scores; a second kernel (1024 threads per row) picks Gamma_q
+//   (and, in the one-call offloaded step, then builds the row's cache map), unless the one-call
+//   decode step ranks it inside its attention launch.  No workgroup ever
 //   waits on another inside a kernel.
 #include "cache_core.h"
 #include "select_core.h"
@@ -93,12 +94,11 @@ __global__ __launch_bounds__(NT) void score_part_kernel(SelectArgs a) {
     score_range<T, D, SPB, NT>(a, row, blk_lo, blk_hi, nullptr, a.scores + (size_t)row * a.scores_stride);
 }
 
-// Gamma_q of rows scored by score_part_kernel (Gamma_e is already in agn_state): one workgroup per row.
+// Gamma_q of row `row` scored by score_part_kernel (Gamma_e is already in agn_state), by the NT
+// threads of one workgroup, in the dynamic LDS `dyn`; writes the row's selection.
 template <int NT>
-__global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
-    extern __shared__ __align__(16) unsigned char dyn[];
-    __shared__ SelectShared<NT> sh;
-    const int row = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void pick_row(const SelectArgs &a, int row, unsigned char *dyn, SelectShared<NT> &sh) {
+    const int tid = threadIdx.x;
     const RowLds L = carve<NT>(dyn, a.n_blocks);
     const float *gscore = a.scores + (size_t)row * a.scores_stride;
     const int32_t *agn = a.agn + (size_t)row * a.ke;
@@ -116,34 +116,26 @@ __global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
     select_query<NT>(a, row, L, sh, false);
 }
 
+// Gamma_q of rows scored by score_part_kernel: one workgroup per row.
+template <int NT>
+__global__ __launch_bounds__(NT) void pick_kernel(SelectArgs a) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ SelectShared<NT> sh;
+    pick_row<NT>(a, blockIdx.x, dyn, sh);
+}
+
 // pick_kernel, then the row's cache map (cache_map_row, by wave 0) from the selection just written:
 // the one-call offloaded step folds the map into the pick instead of launching it on its own.
 template <int NT>
 __global__ __launch_bounds__(NT) void pick_map_kernel(SelectArgs a, CacheArgs c) {
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ SelectShared<NT> sh;
-    const int row = blockIdx.x, tid = threadIdx.x;
-    {
-        const RowLds L = carve<NT>(dyn, a.n_blocks);
-        const float *gscore = a.scores + (size_t)row * a.scores_stride;
-        const int32_t *agn = a.agn + (size_t)row * a.ke;
-        const int id0 = tid < a.ke ? agn[tid] : -1;
-        scores_to_lds<NT>(gscore, a.n_blocks, L);
-        __syncthreads();
-        if (id0 >= 0 && id0 < a.n_blocks) L.inE[id0] = 1;
-        for (int j = tid + NT; j < a.ke; j += NT) {
-            const int id = agn[j];
-            if (id >= 0 && id < a.n_blocks) L.inE[id] = 1;
-        }
-        __syncthreads();
-        select_query<NT>(a, row, L, sh, false);
-    }
+    pick_row<NT>(a, blockIdx.x, dyn, sh);
     // the row's selection (global stores of every wave) is visible to the workgroup after the
     // barrier; the pick's LDS is free again
     __syncthreads();
-    if (tid < 64) cache_map_row(c, row, tid, dyn);
+    if (threadIdx.x < 64) cache_map_row(c, blockIdx.x, threadIdx.x, dyn);
 }
-
 
 template <class K>
 static hipError_t allow_lds(K kern, size_t dyn) {
